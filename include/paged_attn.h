@@ -1,0 +1,178 @@
+/*
+ * paged_attn.h — C ABI of the MI355X (gfx950) paged grouped-query attention library.
+ *
+ * Four operations over a block-paged KV cache:
+ *   kv_page_write       scatter new K/V rows into their pages
+ *   paged_attn_decode   one query row per sequence, split-KV partial softmax
+ *   paged_attn_combine  log-sum-exp merge of the split partials
+ *   paged_attn_prefill  causal attention for packed prompt segments
+ *
+ * Sources (the method these calls implement):
+ *   [crucible-results] crucible, "Paged attention results" (docs/paged-attention-results.md):
+ *       the descriptor, grid and causal-visibility description of the selected prefill kernel;
+ *       the page translation physical_page = request_table[position >> 4], slot = position & 15;
+ *       the GQA map kv_head = query_head / (n_head / n_kv_head).
+ *   [crucible-readme] crucible README: "Paged KV cache and continuous batching" (pool layout,
+ *       offset formula, power-of-two page size), "Split-position attention: implemented, exact,
+ *       and it did not help" (per-chunk partial softmax merged by exp(m_chunk - m_global)),
+ *       the scheduler section on chunked prefill (chunk row r attends to 0 ..= done + r),
+ *       and "What actually runs" (owner and absolute-position arrays route the K/V writes).
+ *   [minfer-d3-6] minfer step 71 "D3-6 GQA q-head batched attention", 3.2 Excerpts A and F:
+ *       the split partition chunk = ceil(nkv / splits), split sp covers
+ *       [sp*chunk, min(nkv, (sp+1)*chunk)); idle splits report max = -inf, sum = 0.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library allocates
+ *     nothing, keeps no state between calls and is re-entrant.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null stream).
+ *     No call synchronises; ordering is stream order, so a kv_page_write enqueued before an
+ *     attention call on the same stream is visible to it.
+ *   - Host scalar arguments are validated before anything is enqueued.  On failure the call
+ *     returns PA_EINVAL (malformed) or PA_EUNSUPPORTED (valid but not built) and enqueues
+ *     nothing.  PA_ELAUNCH reports a HIP launch error.
+ *   - Device-resident metadata (page tables, context lengths, descriptors, positions) is a
+ *     caller contract: page ids in [0, num_pages), lengths and positions inside the table's
+ *     capacity.  The kernels never read or write outside the buffers whose sizes the host
+ *     arguments describe: out-of-range page ids are clamped (attention) or the row is
+ *     skipped (write), and lengths are clamped to max_pages_per_seq * page_size; the
+ *     numerical result for such input is unspecified.
+ *   - Layouts are dense row-major with the innermost dimension last:
+ *       q            [tokens][Hq][D]                    f32
+ *       K/V pages    [num_pages][page_size][Hkv][D]     kv_dtype
+ *       page_table   [rows][max_pages_per_seq]          int32, logical page -> physical page
+ *     Query head h reads KV head h / (Hq / Hkv).
+ *   - Supported: head_dim in {64, 128}; page_size a power of two in [1, 4096];
+ *     Hq a multiple of Hkv with Hq / Hkv <= 64; kv_dtype f32, f16 (IEEE binary16) or bf16.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_EINVAL = -1,        /* malformed argument: null pointer, bad shape, overflow          */
+    PA_EUNSUPPORTED = -2,  /* well-formed but not built: head_dim, dtype, group size          */
+    PA_ELAUNCH = -3        /* the HIP runtime rejected a launch (no device, bad stream, ...)  */
+} pa_status;
+
+/* Short English text for a status code (static storage, never NULL). */
+const char* paged_attn_status_string(int status);
+
+/*
+ * Bytes of split workspace that paged_attn_decode writes and paged_attn_combine reads:
+ *   partial_o  [num_seqs][num_q_heads][num_splits][head_dim] f32
+ *   partial_ml [num_seqs][num_q_heads][num_splits][2]        f32
+ * Returns the sum of both sizes, or 0 if an argument is not positive or the size overflows.
+ */
+size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                         int num_splits);
+
+/*
+ * Split-KV decode: the per-split partial softmax of [crucible-readme] "Split-position
+ * attention" with the split partition of [minfer-d3-6] Excerpt A.
+ *
+ * Sequence b has ctx = context_lens[b] keys, positions 0 .. ctx-1 (ctx counts the current
+ * token, whose K/V the caller has already written).  Its token t lives in physical page
+ * page_table[b][t / page_size], slot t % page_size.  With chunk = ceil(ctx / num_splits),
+ * split s covers tokens [s*chunk, min(ctx, (s+1)*chunk)).  For every query head h and split s:
+ *     score_t = scale * dot(q[b][h][:], K[t][h / (Hq/Hkv)][:])
+ *     m       = max_t score_t                                  (natural-log units)
+ *     l       = sum_t exp(score_t - m)
+ *     O[:]    = sum_t exp(score_t - m) * V[t][h / (Hq/Hkv)][:] (not normalised)
+ * written as partial_ml[b][h][s] = {m, l} and partial_o[b][h][s][:] = O.
+ * An empty split writes m = -INFINITY, l = 0, O = 0.
+ *
+ *   q               [num_seqs][num_q_heads][head_dim] f32, device
+ *   k_pages,v_pages [num_pages][page_size][num_kv_heads][head_dim] kv_dtype, device
+ *   page_table      [num_seqs][max_pages_per_seq] int32, device
+ *   context_lens    [num_seqs] int32, device; 1 <= ctx <= max_pages_per_seq * page_size
+ *                   (ctx <= 0 makes every split empty)
+ *   scale           normally 1/sqrt(head_dim), rounded to f32 by the caller
+ *   num_splits      S in [1, 4096]
+ *   partial_o       [num_seqs][num_q_heads][S][head_dim] f32, device, written
+ *   partial_ml      [num_seqs][num_q_heads][S][2] f32, device, written
+ * num_seqs == 0 is a valid empty call: returns PA_OK and enqueues nothing.
+ */
+int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
+                      pa_dtype kv_dtype, const int32_t* page_table,
+                      const int32_t* context_lens, int num_seqs, int num_q_heads,
+                      int num_kv_heads, int head_dim, int page_size, int num_pages,
+                      int max_pages_per_seq, float scale, int num_splits, float* partial_o,
+                      float* partial_ml, void* stream);
+
+/*
+ * Merge of split partials ([crucible-readme] "Split-position attention": rescale each chunk
+ * by exp(m_chunk - m_global) and merge; [minfer-d3-6] Excerpt F: idle splits weigh zero):
+ *     M      = max over splits with l_s > 0 of m_s
+ *     w_s    = exp(m_s - M) if l_s > 0, else 0
+ *     out[:] = sum_s w_s * O_s[:] / sum_s w_s * l_s
+ * A row whose splits are all empty is written as zeros.
+ *   partial_o, partial_ml as written by paged_attn_decode (same num_seqs/heads/splits/dim)
+ *   out  [num_seqs][num_q_heads][head_dim] f32, device, written
+ */
+int paged_attn_combine(const float* partial_o, const float* partial_ml, int num_seqs,
+                       int num_q_heads, int head_dim, int num_splits, float* out,
+                       void* stream);
+
+/*
+ * Causal packed prefill ([crucible-results] selected-kernel description; [crucible-readme]
+ * scheduler section on chunked prefill).  Segment i is the int32 quadruple
+ *     seg_desc[i] = {packed_start, chunk_len, absolute_start, table_index}
+ * and its packed query row r (0 <= r < chunk_len), at q[packed_start + r], is the token at
+ * absolute position P = absolute_start + r of the sequence whose pages are listed in
+ * page_table[table_index].  It attends to that sequence's positions 0 .. P inclusive:
+ *     out[packed_start + r][h][:] = softmax_t(scale * q.K[t]) . V[t],  t in [0, P]
+ * The caller writes the K/V of every attended position (including the chunk itself) first.
+ * Segments must not overlap in the packed dimension; rows not covered by any segment are
+ * left untouched.
+ *
+ *   q               [total_tokens][num_q_heads][head_dim] f32, device
+ *   k_pages,v_pages [num_pages][page_size][num_kv_heads][head_dim] kv_dtype, device
+ *   page_table      [num_tables][max_pages_per_seq] int32, device
+ *   seg_desc        [num_segs][4] int32, device
+ *   max_chunk_len   host copy of max_i chunk_len (sizes the grid; rows past it are skipped)
+ *   out             [total_tokens][num_q_heads][head_dim] f32, device, written
+ * num_segs == 0 or max_chunk_len == 0 is a valid empty call.
+ */
+int paged_attn_prefill(const float* q, const void* k_pages, const void* v_pages,
+                       pa_dtype kv_dtype, const int32_t* page_table, const int32_t* seg_desc,
+                       int num_segs, int num_tables, int total_tokens, int max_chunk_len,
+                       int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                       int num_pages, int max_pages_per_seq, float scale, float* out,
+                       void* stream);
+
+/*
+ * Page write ([crucible-readme] "Paged KV cache and continuous batching" and "What actually
+ * runs"): for token i with owner row o = token_table_index[i] and absolute position
+ * p = token_position[i], copy the bytes of k_new[i][h][:] to
+ * K[page_table[o][p / page_size]][p % page_size][h][:] for every KV head h, and the same
+ * for V.  No conversion: the copy is bit-exact and every other byte of the pools is left
+ * unchanged.  Tokens whose owner, position or page id is out of range are skipped.  Two
+ * tokens mapping to the same slot in one call race (unspecified which one lands).
+ *
+ *   k_new, v_new        [num_tokens][num_kv_heads][head_dim] kv_dtype, device
+ *   k_pages, v_pages    [num_pages][page_size][num_kv_heads][head_dim] kv_dtype, device
+ *   page_table          [num_tables][max_pages_per_seq] int32, device
+ *   token_table_index   [num_tokens] int32, device
+ *   token_position      [num_tokens] int32, device
+ * num_tokens == 0 is a valid empty call.
+ */
+int kv_page_write(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                  pa_dtype kv_dtype, const int32_t* page_table,
+                  const int32_t* token_table_index, const int32_t* token_position,
+                  int num_tokens, int num_tables, int num_kv_heads, int head_dim,
+                  int page_size, int num_pages, int max_pages_per_seq, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,363 @@
+/*
+ * oracle.c — plain, slow, f64 CPU oracle for paged grouped-query attention.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the bench's CPU-baseline leg
+ * load this library.  It shares no code, header, table or helper with the HIP library; it
+ * is written from the definitions on the source pages, not from the kernels.
+ *
+ * Everything is computed in IEEE double.  Inputs are widened exactly (f32, f16 and bf16 are
+ * all subsets of f64); libm exp() is the only transcendental.  Single-threaded, no SIMD,
+ * no reordering beyond what each definition states: sums run in ascending index order.
+ *
+ * Sources:
+ *  - crucible, "Paged attention results": the reference attention order (full score vector,
+ *    global maximum, exp(score - max), one sum, V accumulated in ascending history order);
+ *    page translation physical_page = request_table[position >> 4], slot = position & 15;
+ *    kv_head = query_head / (n_head / n_kv_head); a packed row at absolute P reads only its
+ *    own request's positions 0..P; descriptors int4[packed_start, chunk_len, absolute_start,
+ *    table_index].
+ *  - crucible README, "Paged KV cache and continuous batching": pool layout and the offset
+ *    formula (here per layer: [num_pages][page_size][Hkv][D]); "Split-position attention":
+ *    per-chunk partial softmax merged by rescaling with exp(m_chunk - m_global), exact;
+ *    "Validating the forward pass": the CPU path is scalar with f64 accumulation.
+ *  - minfer 71 "D3-6 GQA q-head batched attention", 3.2 Excerpt A: chunk = ceil(nkv/splits),
+ *    split sp covers [sp*chunk, min(nkv, sp*chunk + chunk)); Excerpt F: idle splits write
+ *    max = -inf, sum = 0 and weigh zero in the merge.
+ *
+ * Pins: every function here is checked by the CPU tests against things other than itself —
+ * closed forms, a library attention routine, exhaustive dtype decoding against numpy/torch,
+ * brute-force causality, and the causal-position counts the crucible results page prints.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "oracle.h"
+
+/* Planted-mistake hooks, used only by the mutation test (tests/test_oracle_mutants.py):
+ * building with -DORACLE_MUTANT=k compiles mistake k in, to show that some pin fails.
+ * The normal build (ORACLE_MUTANT = 0) contains none of them. */
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+#define MUT(k) (ORACLE_MUTANT == (k))
+
+/* ---------------------------------------------------------------- element decoding */
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t bits) {
+    int sign = (bits >> 15) & 1;
+    int expo = (bits >> 10) & 0x1f;
+    int frac = bits & 0x3ff;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, MUT(1) ? -14 : -24);    /* subnormal: frac * 2^-24 */
+    } else if (expo == 31) {
+        v = frac ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(frac + 1024), expo - 25);    /* (1 + frac/2^10) * 2^(expo-15) */
+    }
+    return sign ? -v : v;
+}
+
+/* bfloat16: the upper 16 bits of an IEEE 754 binary32. */
+double oracle_bf16_to_f64(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double load_elem(const void* base, int dtype, size_t idx) {
+    switch (dtype) {
+        case ORACLE_F32: return (double)((const float*)base)[idx];
+        case ORACLE_F16: return oracle_f16_to_f64(((const uint16_t*)base)[idx]);
+        default:         return oracle_bf16_to_f64(((const uint16_t*)base)[idx]);
+    }
+}
+
+static int elem_size(int dtype) { return dtype == ORACLE_F32 ? 4 : 2; }
+
+/* ---------------------------------------------------------------- paging */
+
+/* Flat element index of K/V[position t][kv head][0] for one sequence's page-table row:
+ * physical page = table_row[t / page_size], slot = t % page_size, pool [P][ps][Hkv][D]. */
+static size_t row_index(const int32_t* table_row, int t, int kv_head, int num_kv_heads,
+                        int head_dim, int page_size) {
+    size_t page = (size_t)table_row[t / page_size];
+    size_t slot = (size_t)((MUT(2) ? t + 1 : t) % page_size);
+    return ((page * (size_t)page_size + slot) * (size_t)num_kv_heads + (size_t)kv_head) *
+           (size_t)head_dim;
+}
+
+/* Contiguous gather of positions 0..n-1 of one KV head into dst[n][D] (f64). */
+static void gather(const void* pages, int dtype, const int32_t* table_row, int n, int kv_head,
+                   int num_kv_heads, int head_dim, int page_size, double* dst) {
+    for (int t = 0; t < n; ++t) {
+        size_t base = row_index(table_row, t, kv_head, num_kv_heads, head_dim, page_size);
+        for (int d = 0; d < head_dim; ++d)
+            dst[(size_t)t * head_dim + d] = load_elem(pages, dtype, base + (size_t)d);
+    }
+}
+
+/* ---------------------------------------------------------------- attention of one row */
+
+/* Exact two-pass softmax attention of one query row over the first n gathered positions:
+ *   s[t]   = scale * sum_d q[d] * K[t][d]           (ascending d)
+ *   m      = max_t s[t]
+ *   p[t]   = exp(s[t] - m),  l = sum_t p[t]         (ascending t)
+ *   out[d] = (sum_t p[t] * V[t][d]) / l             (ascending t)
+ * s is caller scratch of at least n doubles.  n >= 1. */
+static void attend(const float* q, const double* K, const double* V, int n, int head_dim,
+                   double scale, double* s, double* out) {
+    double m = -INFINITY;
+    for (int t = 0; t < n; ++t) {
+        double dot = 0.0;
+        for (int d = 0; d < head_dim; ++d) dot += (double)q[d] * K[(size_t)t * head_dim + d];
+        s[t] = MUT(3) ? dot : scale * dot;
+        if (s[t] > m) m = s[t];
+    }
+    double l = 0.0;
+    for (int t = 0; t < n; ++t) {
+        s[t] = exp(s[t] - m);
+        l += s[t];
+    }
+    for (int d = 0; d < head_dim; ++d) {
+        double acc = 0.0;
+        for (int t = 0; t < n; ++t) acc += s[t] * (MUT(4) ? K : V)[(size_t)t * head_dim + d];
+        out[d] = acc / l;
+    }
+}
+
+static int check_heads(int num_q_heads, int num_kv_heads, int head_dim, int page_size) {
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0) return -1;
+    if (num_q_heads % num_kv_heads != 0) return -1;
+    return 0;
+}
+
+/* ---------------------------------------------------------------- decode */
+
+int oracle_decode(const float* q, const void* k_pages, const void* v_pages, int dtype,
+                  const int32_t* page_table, const int32_t* context_lens, int num_seqs,
+                  int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                  int max_pages_per_seq, float scale, double* out) {
+    if (check_heads(num_q_heads, num_kv_heads, head_dim, page_size)) return -1;
+    const int group = num_q_heads / num_kv_heads;
+    int max_ctx = 1;
+    for (int b = 0; b < num_seqs; ++b) {
+        int n = context_lens[b];
+        if (n < 1 || n > max_pages_per_seq * page_size) return -2;
+        if (n > max_ctx) max_ctx = n;
+    }
+    double* K = malloc(sizeof(double) * (size_t)max_ctx * head_dim);
+    double* V = malloc(sizeof(double) * (size_t)max_ctx * head_dim);
+    double* s = malloc(sizeof(double) * (size_t)max_ctx);
+    if (!K || !V || !s) { free(K); free(V); free(s); return -3; }
+    for (int b = 0; b < num_seqs; ++b) {
+        const int n = context_lens[b];
+        const int32_t* row = page_table + (size_t)b * max_pages_per_seq;
+        for (int g = 0; g < num_kv_heads; ++g) {
+            gather(k_pages, dtype, row, n, g, num_kv_heads, head_dim, page_size, K);
+            gather(v_pages, dtype, row, n, g, num_kv_heads, head_dim, page_size, V);
+            for (int j = 0; j < group; ++j) {
+                const int h = MUT(5) ? j * num_kv_heads + g : g * group + j;
+                attend(q + ((size_t)b * num_q_heads + h) * head_dim, K, V, n, head_dim,
+                       (double)scale, s, out + ((size_t)b * num_q_heads + h) * head_dim);
+            }
+        }
+    }
+    free(K); free(V); free(s);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- split partials */
+
+int oracle_split_range(int n, int num_splits, int split, int* lo, int* hi) {
+    if (num_splits < 1 || split < 0 || split >= num_splits || n < 0) return -1;
+    int chunk = MUT(6) ? n / num_splits : (n + num_splits - 1) / num_splits;
+    int a = split * chunk;
+    int e = a + chunk < n ? a + chunk : n;
+    if (a > n) a = n;
+    if (e < a) e = a;
+    *lo = a;
+    *hi = e;
+    return 0;
+}
+
+int oracle_decode_partials(const float* q, const void* k_pages, const void* v_pages, int dtype,
+                           const int32_t* page_table, const int32_t* context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int page_size, int max_pages_per_seq, float scale, int num_splits,
+                           double* partial_o, double* partial_m, double* partial_l) {
+    if (check_heads(num_q_heads, num_kv_heads, head_dim, page_size) || num_splits < 1)
+        return -1;
+    const int group = num_q_heads / num_kv_heads;
+    int max_ctx = 1;
+    for (int b = 0; b < num_seqs; ++b) {
+        int n = context_lens[b];
+        if (n < 0 || n > max_pages_per_seq * page_size) return -2;
+        if (n > max_ctx) max_ctx = n;
+    }
+    double* K = malloc(sizeof(double) * (size_t)max_ctx * head_dim);
+    double* V = malloc(sizeof(double) * (size_t)max_ctx * head_dim);
+    double* s = malloc(sizeof(double) * (size_t)max_ctx);
+    double* p = malloc(sizeof(double) * (size_t)max_ctx);
+    if (!K || !V || !s || !p) { free(K); free(V); free(s); free(p); return -3; }
+    for (int b = 0; b < num_seqs; ++b) {
+        const int n = context_lens[b];
+        const int32_t* row = page_table + (size_t)b * max_pages_per_seq;
+        for (int g = 0; g < num_kv_heads; ++g) {
+            gather(k_pages, dtype, row, n, g, num_kv_heads, head_dim, page_size, K);
+            gather(v_pages, dtype, row, n, g, num_kv_heads, head_dim, page_size, V);
+            for (int h = g * group; h < (g + 1) * group; ++h) {
+                const float* qh = q + ((size_t)b * num_q_heads + h) * head_dim;
+                for (int t = 0; t < n; ++t) {
+                    double dot = 0.0;
+                    for (int d = 0; d < head_dim; ++d)
+                        dot += (double)qh[d] * K[(size_t)t * head_dim + d];
+                    s[t] = (double)scale * dot;
+                }
+                for (int sp = 0; sp < num_splits; ++sp) {
+                    size_t slot = ((size_t)b * num_q_heads + h) * num_splits + sp;
+                    double* o = partial_o + slot * head_dim;
+                    int lo, hi;
+                    oracle_split_range(n, num_splits, sp, &lo, &hi);
+                    if (lo >= hi) {                       /* idle split */
+                        partial_m[slot] = -INFINITY;
+                        partial_l[slot] = 0.0;
+                        for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
+                        continue;
+                    }
+                    double m = -INFINITY;
+                    for (int t = lo; t < hi; ++t) if (s[t] > m) m = s[t];
+                    double l = 0.0;
+                    for (int t = lo; t < hi; ++t) {
+                        p[t] = exp(s[t] - m);
+                        l += p[t];
+                    }
+                    for (int d = 0; d < head_dim; ++d) {
+                        double acc = 0.0;
+                        for (int t = lo; t < hi; ++t) acc += p[t] * V[(size_t)t * head_dim + d];
+                        o[d] = acc;
+                    }
+                    partial_m[slot] = m;
+                    partial_l[slot] = l;
+                }
+            }
+        }
+    }
+    free(K); free(V); free(s); free(p);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- combine */
+
+int oracle_combine(const double* partial_o, const double* partial_m, const double* partial_l,
+                   int num_seqs, int num_q_heads, int head_dim, int num_splits, double* out) {
+    if (num_splits < 1 || head_dim <= 0) return -1;
+    for (size_t r = 0; r < (size_t)num_seqs * num_q_heads; ++r) {
+        const double* m = partial_m + r * num_splits;
+        const double* l = partial_l + r * num_splits;
+        const double* o = partial_o + r * num_splits * head_dim;
+        double* y = out + r * head_dim;
+        double M = -INFINITY;
+        for (int sp = 0; sp < num_splits; ++sp)
+            if (l[sp] > 0.0 && m[sp] > M) M = m[sp];
+        if (M == -INFINITY) {                             /* every split empty */
+            for (int d = 0; d < head_dim; ++d) y[d] = 0.0;
+            continue;
+        }
+        double L = 0.0;
+        for (int sp = 0; sp < num_splits; ++sp)
+            if (l[sp] > 0.0) L += (MUT(7) ? 1.0 : exp(m[sp] - M)) * l[sp];
+        for (int d = 0; d < head_dim; ++d) {
+            double acc = 0.0;
+            for (int sp = 0; sp < num_splits; ++sp)
+                if (l[sp] > 0.0)
+                    acc += (MUT(7) ? 1.0 : exp(m[sp] - M)) * o[(size_t)sp * head_dim + d];
+            y[d] = acc / L;
+        }
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- prefill */
+
+int oracle_prefill(const float* q, const void* k_pages, const void* v_pages, int dtype,
+                   const int32_t* page_table, const int32_t* seg_desc, int num_segs,
+                   int num_tables, int total_tokens, int num_q_heads, int num_kv_heads,
+                   int head_dim, int page_size, int max_pages_per_seq, float scale,
+                   double* out, int64_t* causal_positions) {
+    if (check_heads(num_q_heads, num_kv_heads, head_dim, page_size)) return -1;
+    const int group = num_q_heads / num_kv_heads;
+    int max_hist = 1;
+    for (int i = 0; i < num_segs; ++i) {
+        const int32_t* dsc = seg_desc + 4 * (size_t)i;
+        int start = dsc[0], len = dsc[1], abs0 = dsc[2], tbl = dsc[3];
+        if (len < 0 || start < 0 || abs0 < 0 || start + len > total_tokens) return -2;
+        if (tbl < 0 || tbl >= num_tables) return -2;
+        if (len > 0 && abs0 + len > max_pages_per_seq * page_size) return -2;
+        if (abs0 + len > max_hist) max_hist = abs0 + len;
+    }
+    double* K = malloc(sizeof(double) * (size_t)max_hist * head_dim);
+    double* V = malloc(sizeof(double) * (size_t)max_hist * head_dim);
+    double* s = malloc(sizeof(double) * (size_t)max_hist);
+    if (!K || !V || !s) { free(K); free(V); free(s); return -3; }
+    int64_t count = 0;
+    for (int i = 0; i < num_segs; ++i) {
+        const int32_t* dsc = seg_desc + 4 * (size_t)i;
+        const int start = dsc[0], len = dsc[1], abs0 = dsc[2];
+        const int32_t* row = page_table + (size_t)(MUT(11) ? 0 : dsc[3]) * max_pages_per_seq;
+        if (len == 0) continue;
+        const int hist = abs0 + len;                      /* positions 0 .. abs0+len-1 */
+        for (int r = 0; r < len; ++r) count += (int64_t)(abs0 + r + 1);
+        for (int g = 0; g < num_kv_heads; ++g) {
+            gather(k_pages, dtype, row, hist, g, num_kv_heads, head_dim, page_size, K);
+            gather(v_pages, dtype, row, hist, g, num_kv_heads, head_dim, page_size, V);
+            for (int h = g * group; h < (g + 1) * group; ++h) {
+                for (int r = 0; r < len; ++r) {
+                    const int P = (MUT(9) ? 0 : abs0) + r;  /* absolute position of the row */
+                    const size_t tok = (size_t)start + r;
+                    attend(q + (tok * num_q_heads + h) * head_dim, K, V, MUT(8) ? P : P + 1,
+                           head_dim,
+                           (double)scale, s, out + (tok * num_q_heads + h) * head_dim);
+                }
+            }
+        }
+    }
+    if (causal_positions) *causal_positions = count;
+    free(K); free(V); free(s);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- page write */
+
+int oracle_kv_write(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                    int dtype, const int32_t* page_table, const int32_t* token_table_index,
+                    const int32_t* token_position, int num_tokens, int num_tables,
+                    int num_kv_heads, int head_dim, int page_size, int num_pages,
+                    int max_pages_per_seq) {
+    if (num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0) return -1;
+    const size_t row_bytes = (size_t)num_kv_heads * head_dim * elem_size(dtype);
+    for (int i = 0; i < num_tokens; ++i) {
+        int owner = token_table_index[i];
+        int pos = token_position[i];
+        if (owner < 0 || owner >= num_tables) continue;
+        if (pos < 0 || pos >= max_pages_per_seq * page_size) continue;
+        int page = page_table[(size_t)owner * max_pages_per_seq + pos / page_size];
+        if (page < 0 || page >= num_pages) continue;
+        size_t dst = ((size_t)page * page_size + (size_t)((MUT(10) ? pos + 1 : pos) % page_size)) *
+                     row_bytes;
+        memcpy((char*)k_pages + dst, (const char*)k_new + (size_t)i * row_bytes, row_bytes);
+        memcpy((char*)v_pages + dst, (const char*)v_new + (size_t)i * row_bytes, row_bytes);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- helpers for the tests */
+
+/* dst[i] = exact f64 value of element i of src (dtype f32, f16 or bf16). */
+void oracle_widen(int dtype, const void* src, int64_t n, double* dst) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = load_elem(src, dtype, (size_t)i);
+}

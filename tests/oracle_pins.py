@@ -1,0 +1,496 @@
+"""Pins of the f64 oracle to things other than itself.
+
+Every ``pin_*`` function takes an oracle instance and raises AssertionError on failure.
+``test_oracle_pins.py`` runs them on the real oracle; ``test_oracle_mutants.py`` runs them on
+builds with planted mistakes and requires that each mistake fails at least one pin.
+
+What pins what:
+  * element decoding   — exhaustive over all 65,536 bit patterns against numpy (f16) and
+                         torch (bf16) conversions;
+  * attention          — a library routine (torch scaled_dot_product_attention in float64)
+                         on contiguous tensors, with K/V repeated per group
+                         (crucible README, "Tests": test_gqa_paths_match pins GQA this way);
+                         closed forms: a two-key sigmoid, context 1 returns V[0], q = 0
+                         returns the mean of V;
+  * paging             — pools built from contiguous tensors by numpy reshaping (not by the
+                         oracle's index formula); page-permutation invariance, bit-exact
+                         (crucible README: paging moves storage, not arithmetic);
+  * GQA                — equals MHA with K/V repeated per group, bit-exact;
+  * split-KV + merge   — equals the unsplit result (crucible README, "Split-position
+                         attention": it is exact); the partition boundary the minfer D3-6
+                         page prints (golden file); idle splits weigh zero;
+  * causality          — brute force on tiny inputs against the library routine with a
+                         causal mask; editing token t leaves earlier rows bit-identical
+                         (crucible README, "Tests": test_causality); prefill rows equal decode;
+  * causal extent      — the sums of causal positions the crucible results page prints for
+                         its benchmark shapes (golden file);
+  * page write         — against numpy reshaping of the contiguous rows, byte-exact.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+from compare import assert_bitwise, assert_within
+from paged_gqa_attention_decode_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def ref_widen(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Library conversions of stored values to float64 (independent of the oracle)."""
+    if dtype == "f32":
+        return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(arr, dtype=np.uint16).view(np.float16).astype(np.float64)
+    t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def random_storage(rng, shape, dtype, scale=1.0):
+    return wl.to_storage(scale * rng.standard_normal(shape).astype(np.float32), dtype)
+
+
+def build_paged(rng, seqs_k, seqs_v, page_size, dtype, spare_pages=3):
+    """Place each sequence's contiguous [n, Hkv, D] rows into a shared pool at random
+    physical pages, by reshaping; unused bytes are NaN.  Returns (k_pool, v_pool, table)."""
+    hkv, d = seqs_k[0].shape[1:]
+    need = [-(-k.shape[0] // page_size) for k in seqs_k]
+    num_pages = sum(need) + spare_pages
+    perm = rng.permutation(num_pages)
+    nan = wl.nan_value(dtype)
+    k_pool = np.full((num_pages, page_size, hkv, d), nan, dtype=wl.storage_dtype(dtype))
+    v_pool = k_pool.copy()
+    table = np.full((len(seqs_k), max(need)), -1, dtype=np.int32)
+    c = 0
+    for b, (k, v) in enumerate(zip(seqs_k, seqs_v)):
+        pages = perm[c:c + need[b]]
+        c += need[b]
+        pad_k = np.full((need[b] * page_size, hkv, d), nan, dtype=k_pool.dtype)
+        pad_v = pad_k.copy()
+        pad_k[: k.shape[0]] = k
+        pad_v[: v.shape[0]] = v
+        k_pool[pages] = pad_k.reshape(need[b], page_size, hkv, d)
+        v_pool[pages] = pad_v.reshape(need[b], page_size, hkv, d)
+        table[b, : need[b]] = pages
+    return k_pool, v_pool, table
+
+
+def sdpa(q, k, v, scale, mask=None, is_causal=False):
+    """torch float64 attention. q [Hq, Lq, D]; k, v [Hkv, Lk, D]; K/V repeated per group."""
+    hq, hkv = q.shape[0], k.shape[0]
+    kt = torch.from_numpy(k).repeat_interleave(hq // hkv, dim=0)
+    vt = torch.from_numpy(v).repeat_interleave(hq // hkv, dim=0)
+    m = None if mask is None else torch.from_numpy(mask)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], kt[None], vt[None], attn_mask=m, is_causal=is_causal,
+        scale=scale)
+    return out[0].numpy()
+
+
+def _decode_setup(rng, *, batch, hq, hkv, d, ps, dtype, ctxs, qscale=1.0):
+    ks = [random_storage(rng, (n, hkv, d), dtype) for n in ctxs]
+    vs = [random_storage(rng, (n, hkv, d), dtype) for n in ctxs]
+    kp, vp, table = build_paged(rng, ks, vs, ps, dtype)
+    q = (qscale * rng.standard_normal((batch, hq, d))).astype(np.float32)
+    return q, ks, vs, kp, vp, table, np.asarray(ctxs, dtype=np.int32)
+
+
+# ----------------------------------------------------------------------------- decoding
+
+def pin_f16_exhaustive(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.widen(bits, "f16")
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "f16 NaN set differs"
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]), "f16 decoding differs from numpy"
+
+
+def pin_bf16_exhaustive(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.widen(bits, "bf16")
+    ref = ref_widen(bits, "bf16")
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), "bf16 NaN set differs"
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]), "bf16 decoding differs from torch"
+
+
+# ----------------------------------------------------------------------------- closed forms
+
+def pin_two_key_sigmoid(orc):
+    """One head, D=1, keys k=[0, 2], values [0, 1], q=1, scale 0.5: scores [0, 1], so the
+    output is the weight of the second key, 1 / (1 + e^-1)."""
+    kp = np.array([0.0, 2.0], np.float32).reshape(1, 2, 1, 1)
+    vp = np.array([0.0, 1.0], np.float32).reshape(1, 2, 1, 1)
+    q = np.ones((1, 1, 1), np.float32)
+    out = orc.decode(q, kp, vp, "f32", np.zeros((1, 1), np.int32), np.array([2], np.int32),
+                     0.5)
+    expect = 1.0 / (1.0 + math.exp(-1.0))
+    assert abs(out[0, 0, 0] - expect) < 1e-15, (out[0, 0, 0], expect)
+
+
+def pin_ctx1_returns_v0(orc):
+    rng = wl.rng_for(101)
+    for dtype in ("f32", "f16", "bf16"):
+        for hq, hkv, d in ((8, 2, 64), (5, 1, 128), (3, 3, 64)):
+            q, ks, vs, kp, vp, table, ctx = _decode_setup(
+                rng, batch=2, hq=hq, hkv=hkv, d=d, ps=16, dtype=dtype, ctxs=[1, 1])
+            out = orc.decode(q, kp, vp, dtype, table, ctx, 1.0 / math.sqrt(d))
+            for b in range(2):
+                v0 = ref_widen(vs[b][0], dtype)               # [Hkv, D]
+                expect = np.repeat(v0, hq // hkv, axis=0)
+                assert_bitwise(out[b], expect, f"ctx=1 {dtype} {hq}/{hkv}")
+
+
+def pin_zero_query_mean(orc):
+    rng = wl.rng_for(102)
+    for dtype in ("f32", "bf16"):
+        q, ks, vs, kp, vp, table, ctx = _decode_setup(
+            rng, batch=2, hq=4, hkv=2, d=64, ps=16, dtype=dtype, ctxs=[37, 300])
+        q[:] = 0.0
+        out = orc.decode(q, kp, vp, dtype, table, ctx, 0.125)
+        for b in range(2):
+            mean = ref_widen(vs[b], dtype).mean(axis=0)       # [Hkv, D]
+            assert_within(out[b], np.repeat(mean, 2, axis=0), 1e-13, 0, "q=0 mean")
+
+
+# ----------------------------------------------------------------------------- library pin
+
+def pin_decode_vs_sdpa(orc):
+    rng = wl.rng_for(103)
+    cases = [
+        # batch, hq, hkv, d, ps, dtype, ctxs
+        (1, 8, 2, 64, 16, "f32", [256]),
+        (2, 40, 8, 128, 16, "f16", [97, 300]),
+        (2, 28, 4, 128, 16, "f16", [1, 65]),
+        (3, 64, 8, 128, 32, "bf16", [64, 31, 129]),
+        (1, 12, 12, 64, 1, "f32", [19]),
+        (2, 12, 3, 64, 8, "bf16", [17, 40]),
+    ]
+    for batch, hq, hkv, d, ps, dtype, ctxs in cases:
+        q, ks, vs, kp, vp, table, ctx = _decode_setup(
+            rng, batch=batch, hq=hq, hkv=hkv, d=d, ps=ps, dtype=dtype, ctxs=ctxs)
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+        out = orc.decode(q, kp, vp, dtype, table, ctx, scale)
+        for b in range(batch):
+            k = ref_widen(ks[b], dtype).transpose(1, 0, 2).copy()   # [Hkv, n, D]
+            v = ref_widen(vs[b], dtype).transpose(1, 0, 2).copy()
+            ref = sdpa(q[b].astype(np.float64)[:, None, :], k, v, scale)[:, 0, :]
+            assert_within(out[b], ref, 1e-12, 1e-12, f"decode vs sdpa {hq}/{hkv} {dtype}")
+
+
+def pin_outlier_data_vs_sdpa(orc):
+    """The outlier-scale generators of the minfer D3-6 page, 4. Verification (|q| ~ 57,
+    |v| ~ 144), on the 14B geometry: still within 1e-12 of the library routine."""
+    hq, hkv, d, n = 40, 8, 128, 300
+    qs = np.array([(((i * 37) % 19) / 5.0 - 1.9) * 30.0 for i in range(hq * d)], np.float32)
+    vs = np.array([(((i * 57) % 11) / 3.0 - 1.8) * 80.0 for i in range(n * hkv * d)],
+                  np.float32)
+    rng = wl.rng_for(104)
+    k = wl.to_storage(rng.standard_normal((n, hkv, d)).astype(np.float32), "f16")
+    v = wl.to_storage(vs.reshape(n, hkv, d), "f16")
+    kp, vp, table = build_paged(rng, [k], [v], 16, "f16")
+    q = qs.reshape(1, hq, d)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    out = orc.decode(q, kp, vp, "f16", table, np.array([n], np.int32), scale)
+    ref = sdpa(q[0].astype(np.float64)[:, None, :], ref_widen(k, "f16").transpose(1, 0, 2).copy(),
+               ref_widen(v, "f16").transpose(1, 0, 2).copy(), scale)[:, 0, :]
+    assert_within(out[0], ref, 1e-10, 1e-12, "outlier decode vs sdpa")
+
+
+# ----------------------------------------------------------------------------- invariants
+
+def pin_page_permutation(orc):
+    """Relabelling physical pages (and the table with them) changes no bit."""
+    rng = wl.rng_for(105)
+    q, ks, vs, kp, vp, table, ctx = _decode_setup(
+        rng, batch=3, hq=8, hkv=2, d=64, ps=16, dtype="bf16", ctxs=[200, 17, 64])
+    base = orc.decode(q, kp, vp, "bf16", table, ctx, 0.125)
+    pi = rng.permutation(kp.shape[0])
+    kp2 = np.empty_like(kp)
+    vp2 = np.empty_like(vp)
+    kp2[pi] = kp
+    vp2[pi] = vp
+    table2 = np.where(table >= 0, pi[np.maximum(table, 0)], -1).astype(np.int32)
+    out = orc.decode(q, kp2, vp2, "bf16", table2, ctx, 0.125)
+    assert_bitwise(out, base, "page permutation")
+
+
+def pin_gqa_equals_mha(orc):
+    rng = wl.rng_for(106)
+    for g in (4, 5, 8):
+        hkv, d = 2, 128
+        q, ks, vs, kp, vp, table, ctx = _decode_setup(
+            rng, batch=2, hq=hkv * g, hkv=hkv, d=d, ps=16, dtype="f16", ctxs=[99, 130])
+        gqa = orc.decode(q, kp, vp, "f16", table, ctx, 0.0883883461356163)
+        kp_m = np.repeat(kp, g, axis=2)
+        vp_m = np.repeat(vp, g, axis=2)
+        mha = orc.decode(q, kp_m, vp_m, "f16", table, ctx, 0.0883883461356163)
+        assert_bitwise(gqa, mha, f"GQA g={g} vs repeated-KV MHA")
+
+
+def pin_batch_invariance(orc):
+    rng = wl.rng_for(107)
+    q, ks, vs, kp, vp, table, ctx = _decode_setup(
+        rng, batch=4, hq=8, hkv=2, d=64, ps=16, dtype="f32", ctxs=[50, 3, 129, 16])
+    full = orc.decode(q, kp, vp, "f32", table, ctx, 0.125)
+    for b in range(4):
+        alone = orc.decode(q[b:b + 1], kp, vp, "f32", table[b:b + 1], ctx[b:b + 1], 0.125)
+        assert_bitwise(alone[0], full[b], f"batch invariance b={b}")
+    rev = orc.decode(q[::-1].copy(), kp, vp, "f32", table[::-1].copy(), ctx[::-1].copy(), 0.125)
+    assert_bitwise(rev[::-1], full, "reversed batch")
+
+
+def pin_future_poison(orc):
+    """Never-read bytes are NaN in the generator's cases: outputs are finite and equal to
+    the same case with those bytes holding ordinary values."""
+    w = wl.WORKLOADS["decode_hq8_hkv2_d64_ctx256_f32"]
+    clean = wl.workload_decode_case(w, poison=False, new_token_in_pool=True)
+    dirty = wl.workload_decode_case(w, poison=True, new_token_in_pool=True)
+    a = orc.decode(clean.q, clean.k_pages, clean.v_pages, "f32", clean.page_table,
+                   clean.context_lens, clean.scale)
+    b = orc.decode(dirty.q, dirty.k_pages, dirty.v_pages, "f32", dirty.page_table,
+                   dirty.context_lens, dirty.scale)
+    assert np.isfinite(b).all(), "poison leaked into the output"
+    assert_bitwise(b, a, "future poison")
+
+
+# ----------------------------------------------------------------------------- split-KV
+
+def pin_split_rule_golden(orc):
+    rows = _golden_rows("split_boundary.txt")
+    for nkv, splits, rpw in rows:
+        nkv, splits, rpw = int(nkv), int(splits), int(rpw)
+        lo, hi = orc.split_range(nkv, splits, 0)
+        chunk = hi - lo
+        assert -(-chunk // 4) == rpw, (nkv, chunk, rpw)
+
+
+def pin_split_partition(orc):
+    for n in (1, 2, 31, 32, 33, 100, 3254, 1641):
+        for s in (1, 2, 7, 16, 32, 64, n, n + 5):
+            ranges = [orc.split_range(n, s, i) for i in range(s)]
+            covered = []
+            for lo, hi in ranges:
+                covered.extend(range(lo, hi))
+            assert covered == list(range(n)), (n, s)
+            sizes = [hi - lo for lo, hi in ranges if hi > lo]
+            assert len(set(sizes[:-1])) <= 1 and sizes[-1] <= sizes[0], (n, s, sizes)
+
+
+def pin_split_combine_equals_unsplit(orc):
+    rng = wl.rng_for(108)
+    q, ks, vs, kp, vp, table, ctx = _decode_setup(
+        rng, batch=3, hq=10, hkv=2, d=64, ps=16, dtype="bf16", ctxs=[257, 7, 1000])
+    full = orc.decode(q, kp, vp, "bf16", table, ctx, 0.125)
+    for s in (1, 2, 7, 32, 257, 1005):
+        po, pm, pl = orc.decode_partials(q, kp, vp, "bf16", table, ctx, 0.125, s)
+        merged = orc.combine(po, pm, pl)
+        assert_within(merged, full, 1e-12, 1e-12, f"split {s} + combine vs unsplit")
+        if s == 1:
+            assert_within(po[:, :, 0, :] / pl[:, :, 0, None], full, 1e-13, 1e-13, "S=1 O/l")
+
+
+def pin_idle_splits(orc):
+    rng = wl.rng_for(109)
+    q, ks, vs, kp, vp, table, ctx = _decode_setup(
+        rng, batch=1, hq=4, hkv=1, d=64, ps=16, dtype="f32", ctxs=[5])
+    po, pm, pl = orc.decode_partials(q, kp, vp, "f32", table, ctx, 0.125, 8)
+    assert np.all(pm[..., 5:] == -np.inf) and np.all(pl[..., 5:] == 0.0)
+    assert np.all(po[..., 5:, :] == 0.0)
+    assert np.all(pl[..., :5] == 1.0)                      # one row per split: exp(0) = 1
+    o = np.zeros((1, 2, 4, 8))
+    m = np.full((1, 2, 4), -np.inf)
+    l = np.zeros((1, 2, 4))
+    assert np.all(orc.combine(o, m, l) == 0.0), "all-idle rows must give zeros"
+
+
+def pin_combine_invariances(orc):
+    rng = wl.rng_for(110)
+    o, ml = wl.make_partials(rng, batch=2, hq=3, head_dim=16, num_splits=9, all_empty_rows=1)
+    m, l = ml[..., 0].astype(np.float64), ml[..., 1].astype(np.float64)
+    o = o.astype(np.float64)
+    base = orc.combine(o, m, l)
+    c = 3.75
+    shifted = orc.combine(o * math.exp(-c), m + c, l * math.exp(-c))
+    assert_within(shifted, base, 1e-13, 1e-12, "combine shift invariance")
+    perm = rng.permutation(9)
+    assert_within(orc.combine(o[:, :, perm], m[:, :, perm], l[:, :, perm]), base, 1e-13, 1e-12,
+                  "combine split-order invariance")
+    one = np.zeros_like(o)
+    one[:, :, 4] = o[:, :, 4]
+    m1 = np.full_like(m, -np.inf)
+    m1[:, :, 4] = m[:, :, 4]
+    l1 = np.zeros_like(l)
+    l1[:, :, 4] = l[:, :, 4]
+    got = orc.combine(one, m1, l1)
+    live = l[:, :, 4] > 0
+    with np.errstate(invalid="ignore", divide="ignore"):
+        expect = o[:, :, 4] / l[:, :, 4, None]
+    assert_within(got[live], expect[live], 1e-15, 1e-15, "single live split")
+
+
+# ----------------------------------------------------------------------------- prefill
+
+def _prefill_setup(rng, hq, hkv, d, ps, dtype, starts, lens):
+    ks = [random_storage(rng, (s + n, hkv, d), dtype) for s, n in zip(starts, lens)]
+    vs = [random_storage(rng, (s + n, hkv, d), dtype) for s, n in zip(starts, lens)]
+    kp, vp, table = build_paged(rng, ks, vs, ps, dtype)
+    total = sum(lens)
+    q = rng.standard_normal((total, hq, d)).astype(np.float32)
+    desc = []
+    c = 0
+    for i, (s, n) in enumerate(zip(starts, lens)):
+        desc.append([c, n, s, i])
+        c += n
+    return q, ks, vs, kp, vp, table, np.array(desc, np.int32).reshape(-1, 4)
+
+
+def pin_prefill_vs_sdpa_causal(orc):
+    rng = wl.rng_for(111)
+    for hq, hkv, d, ps, dtype, starts, lens in (
+            (4, 4, 64, 16, "f32", [0], [70]),
+            (12, 3, 64, 16, "f32", [0, 63, 5], [17, 40, 1]),
+            (8, 2, 128, 32, "bf16", [33, 0], [20, 9]),
+            (2, 1, 64, 4, "f16", [0, 3], [8, 5])):
+        q, ks, vs, kp, vp, table, desc = _prefill_setup(rng, hq, hkv, d, ps, dtype, starts,
+                                                        lens)
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+        out, _ = orc.prefill(q, kp, vp, dtype, table, desc, scale)
+        for i, (start, n) in enumerate(zip(starts, lens)):
+            rows = slice(desc[i, 0], desc[i, 0] + n)
+            qq = q[rows].astype(np.float64).transpose(1, 0, 2).copy()          # [Hq, n, D]
+            k = ref_widen(ks[i], dtype).transpose(1, 0, 2).copy()              # [Hkv, s+n, D]
+            v = ref_widen(vs[i], dtype).transpose(1, 0, 2).copy()
+            if start == 0:
+                ref = sdpa(qq, k, v, scale, is_causal=True)
+            else:
+                mask = np.tril(np.ones((n, start + n), dtype=bool), k=start)
+                ref = sdpa(qq, k, v, scale, mask=mask)
+            assert_within(out[rows], ref.transpose(1, 0, 2), 1e-12, 1e-12,
+                          f"prefill vs sdpa seg {i}")
+
+
+def pin_prefill_rows_equal_decode(orc):
+    rng = wl.rng_for(112)
+    q, ks, vs, kp, vp, table, desc = _prefill_setup(rng, 8, 2, 64, 16, "bf16", [21, 0],
+                                                    [12, 33])
+    out, _ = orc.prefill(q, kp, vp, "bf16", table, desc, 0.125)
+    for i in range(2):
+        start, n = int(desc[i, 2]), int(desc[i, 1])
+        for r in range(n):
+            row = int(desc[i, 0]) + r
+            dec = orc.decode(q[row:row + 1], kp, vp, "bf16", table[i:i + 1],
+                             np.array([start + r + 1], np.int32), 0.125)
+            assert_bitwise(out[row], dec[0], f"prefill row {row} vs decode")
+
+
+def pin_causality_brute_force(orc):
+    """T <= 8: editing token t (its q, K and V) leaves every earlier row bit-identical and
+    changes every later row."""
+    for T in (1, 2, 5, 8):
+        rng = wl.rng_for(113)
+        q = rng.standard_normal((T, 2, 64)).astype(np.float32)
+        k = random_storage(rng, (T, 1, 64), "f32")
+        v = random_storage(rng, (T, 1, 64), "f32")
+        desc = np.array([[0, T, 0, 0]], np.int32)
+        kp, vp, table = build_paged(wl.rng_for(1130), [k], [v], 4, "f32")
+        base, _ = orc.prefill(q, kp, vp, "f32", table, desc, 0.125)
+        for t in range(T):
+            q2, k2, v2 = q.copy(), k.copy(), v.copy()
+            q2[t] += 1.0
+            k2[t] += 1.0
+            v2[t] += 1.0
+            kp2, vp2, table2 = build_paged(wl.rng_for(1130), [k2], [v2], 4, "f32")
+            edited, _ = orc.prefill(q2, kp2, vp2, "f32", table2, desc, 0.125)
+            assert_bitwise(edited[:t], base[:t], f"T={T} edit at {t}: earlier rows")
+            assert np.all(edited[t:] != base[t:]), f"T={T} edit at {t}: later rows unchanged"
+
+
+def pin_causal_position_counts(orc):
+    """The oracle's causal extent reproduces the crucible results page's printed sums."""
+    for name, starts, lens, printed in _golden_causal():
+        rng = wl.rng_for(114)
+        q, ks, vs, kp, vp, table, desc = _prefill_setup(rng, 1, 1, 8, 16, "f32", starts, lens)
+        _, count = orc.prefill(q, kp, vp, "f32", table, desc, 0.125)
+        assert count == printed, (name, count, printed)
+
+
+# ----------------------------------------------------------------------------- page write
+
+def pin_kv_write_vs_reshape(orc):
+    """Writing every position of two sequences token by token equals placing the rows by
+    reshaping; bytes of other pages keep their poison."""
+    rng = wl.rng_for(115)
+    for dtype, ps, hkv, d in (("f32", 16, 12, 64), ("bf16", 32, 8, 128), ("f16", 1, 2, 64)):
+        lens = [45, 16]
+        ks = [random_storage(rng, (n, hkv, d), dtype) for n in lens]
+        vs = [random_storage(rng, (n, hkv, d), dtype) for n in lens]
+        ref_k, ref_v, table = build_paged(rng, ks, vs, ps, dtype)
+        empty = np.full_like(ref_k, wl.nan_value(dtype))
+        owner = np.concatenate([np.full(n, i, np.int32) for i, n in enumerate(lens)])
+        pos = np.concatenate([np.arange(n, dtype=np.int32) for n in lens])
+        order = rng.permutation(owner.size)
+        k_new = np.concatenate(ks)[order]
+        v_new = np.concatenate(vs)[order]
+        got_k, got_v = orc.kv_write(k_new, v_new, empty, empty, dtype, table, owner[order],
+                                    pos[order])
+        assert_bitwise(got_k, ref_k, f"kv_write K {dtype}")
+        assert_bitwise(got_v, ref_v, f"kv_write V {dtype}")
+
+
+def pin_kv_write_skips_invalid(orc):
+    rng = wl.rng_for(116)
+    pool = random_storage(rng, (4, 16, 2, 64), "bf16")
+    table = np.array([[2, 0], [1, 9]], np.int32)        # page 9 does not exist
+    new = random_storage(rng, (4, 2, 64), "bf16")
+    owner = np.array([0, 1, 5, -1], np.int32)
+    pos = np.array([40, 17, 0, 0], np.int32)            # 40 past capacity; 17 -> page 9
+    k, v = orc.kv_write(new, new, pool, pool, "bf16", table, owner, pos)
+    assert_bitwise(k, pool, "invalid tokens must not write")
+    assert_bitwise(v, pool, "invalid tokens must not write")
+
+
+# ----------------------------------------------------------------------------- registry
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([c.strip() for c in line.split("|")])
+    return rows
+
+
+def _expand(field):
+    out = []
+    for part in field.split(","):
+        if "*" in part:
+            v, n = part.split("*")
+            out.extend([int(v)] * int(n))
+        else:
+            out.append(int(part))
+    return out
+
+
+def _golden_causal():
+    return [(r[0], _expand(r[1]), _expand(r[2]), int(r[3]))
+            for r in _golden_rows("causal_positions.txt")]
+
+
+PINS = [
+    pin_f16_exhaustive, pin_bf16_exhaustive, pin_two_key_sigmoid, pin_ctx1_returns_v0,
+    pin_zero_query_mean, pin_decode_vs_sdpa, pin_outlier_data_vs_sdpa, pin_page_permutation,
+    pin_gqa_equals_mha, pin_batch_invariance, pin_future_poison, pin_split_rule_golden,
+    pin_split_partition, pin_split_combine_equals_unsplit, pin_idle_splits,
+    pin_combine_invariances, pin_prefill_vs_sdpa_causal, pin_prefill_rows_equal_decode,
+    pin_causality_brute_force, pin_causal_position_counts, pin_kv_write_vs_reshape,
+    pin_kv_write_skips_invalid,
+]
