@@ -1,0 +1,227 @@
+// api.hip — the C ABI of include/paged_attn.h: host-side validation, then one launch per
+// kernel on the caller's stream.  No allocation, no synchronisation, no state.
+//
+// Every host scalar is checked before anything is enqueued (crucible, "Paged attention
+// results": malformed shapes, overflow and bad indices are rejected before device access).
+// Device-resident metadata is not read here: that would need a device-to-host copy and a
+// synchronisation.  The kernels instead keep every access inside the buffers the host
+// arguments describe (clamped page ids, clamped lengths, skipped rows).
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/paged_attn.h"
+#include "common.h"
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+constexpr int kMaxGridYZ = 65535;
+constexpr int kMaxSplits = 4096;
+constexpr int kMaxGroup = 64;
+constexpr int kMaxHeadsPerWg = 8;
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return s;
+}
+
+bool valid_dtype(int d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+
+int elem_bytes(int d) { return d == PA_F32 ? 4 : 2; }
+
+// Shape checks shared by the calls that read K/V pages.
+int check_pages(int kv_dtype, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                int num_pages, int max_pages_per_seq) {
+    if (!valid_dtype(kv_dtype)) return PA_EINVAL;
+    if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0)
+        return PA_EINVAL;
+    if (head_dim < 1 || page_size < 1 || num_pages < 1 || max_pages_per_seq < 1)
+        return PA_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return PA_EUNSUPPORTED;
+    if (!is_pow2(page_size) || page_size > 4096) return PA_EUNSUPPORTED;
+    if (num_q_heads / num_kv_heads > kMaxGroup) return PA_EUNSUPPORTED;
+    if ((int64_t)max_pages_per_seq * page_size > kI32Max) return PA_EINVAL;
+    if ((int64_t)num_pages * page_size > kI32Max) return PA_EINVAL;
+    return PA_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* paged_attn_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_EINVAL: return "invalid argument";
+        case PA_EUNSUPPORTED: return "unsupported configuration";
+        case PA_ELAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                         int num_splits) {
+    if (num_seqs < 1 || num_q_heads < 1 || head_dim < 1 || num_splits < 1) return 0;
+    const unsigned __int128 rows =
+        (unsigned __int128)num_seqs * (unsigned __int128)num_q_heads * (unsigned)num_splits;
+    const unsigned __int128 bytes = rows * (unsigned __int128)(head_dim + 2) * 4u;
+    if (bytes > (unsigned __int128)SIZE_MAX / 2) return 0;
+    return (size_t)bytes;
+}
+
+int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
+                      pa_dtype kv_dtype, const int32_t* page_table,
+                      const int32_t* context_lens, int num_seqs, int num_q_heads,
+                      int num_kv_heads, int head_dim, int page_size, int num_pages,
+                      int max_pages_per_seq, float scale, int num_splits, float* partial_o,
+                      float* partial_ml, void* stream) {
+    if (num_seqs < 0) return PA_EINVAL;
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_pages || !v_pages || !page_table || !context_lens || !partial_o || !partial_ml)
+        return PA_EINVAL;
+    int rc = check_pages(kv_dtype, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                         max_pages_per_seq);
+    if (rc != PA_OK) return rc;
+    if (num_splits < 1) return PA_EINVAL;
+    if (num_splits > kMaxSplits) return PA_EUNSUPPORTED;
+    if (!isfinite(scale)) return PA_EINVAL;
+    if (num_seqs > kMaxGridYZ) return PA_EUNSUPPORTED;
+    if ((int64_t)num_seqs * max_pages_per_seq > kI32Max ||
+        (int64_t)num_seqs * num_q_heads * num_splits * head_dim > kI32Max * 4LL)
+        return PA_EINVAL;
+
+    const int group = num_q_heads / num_kv_heads;
+    const int head_groups = (group + kMaxHeadsPerWg - 1) / kMaxHeadsPerWg;
+    const int heads_per_wg = (group + head_groups - 1) / head_groups;
+    if ((int64_t)num_kv_heads * head_groups > kMaxGridYZ) return PA_EUNSUPPORTED;
+
+    pa::DecodeArgs a;
+    a.q = q;
+    a.k_pages = k_pages;
+    a.v_pages = v_pages;
+    a.page_table = page_table;
+    a.context_lens = context_lens;
+    a.partial_o = partial_o;
+    a.partial_ml = partial_ml;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = group;
+    a.head_groups = head_groups;
+    a.heads_per_wg = heads_per_wg;
+    a.page_shift = ilog2(page_size);
+    a.num_pages = num_pages;
+    a.max_pages = max_pages_per_seq;
+    a.num_splits = num_splits;
+    a.qscale = scale * pa::kLog2e;
+
+    // Waves per workgroup: enough that one window pass covers the split's rows when the
+    // context is at the table's capacity (a host-side bound; lengths live on the device).
+    const int rows_per_wave_window = (64 / (head_dim * elem_bytes(kv_dtype) / 16)) * 4;
+    const int64_t cap = (int64_t)max_pages_per_seq * page_size;
+    const int64_t chunk = (cap + num_splits - 1) / num_splits;
+    int waves = (int)((chunk + rows_per_wave_window - 1) / rows_per_wave_window);
+    waves = waves < 1 ? 1 : (waves > 8 ? 8 : waves);
+    return launched(pa::launch_decode(a, kv_dtype, head_dim, waves, (hipStream_t)stream));
+}
+
+int paged_attn_combine(const float* partial_o, const float* partial_ml, int num_seqs,
+                       int num_q_heads, int head_dim, int num_splits, float* out,
+                       void* stream) {
+    if (num_seqs < 0 || num_q_heads < 1 || num_splits < 1 || head_dim < 1) return PA_EINVAL;
+    if (num_seqs == 0) return PA_OK;
+    if (!partial_o || !partial_ml || !out) return PA_EINVAL;
+    if (head_dim != 64 && head_dim != 128) return PA_EUNSUPPORTED;
+    if (num_splits > kMaxSplits) return PA_EUNSUPPORTED;
+    if ((int64_t)num_seqs * num_q_heads > kI32Max / 32) return PA_EINVAL;
+    pa::CombineArgs a;
+    a.partial_o = partial_o;
+    a.partial_ml = partial_ml;
+    a.out = out;
+    a.rows = num_seqs * num_q_heads;
+    a.num_splits = num_splits;
+    return launched(pa::launch_combine(a, head_dim, (hipStream_t)stream));
+}
+
+int paged_attn_prefill(const float* q, const void* k_pages, const void* v_pages,
+                       pa_dtype kv_dtype, const int32_t* page_table, const int32_t* seg_desc,
+                       int num_segs, int num_tables, int total_tokens, int max_chunk_len,
+                       int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                       int num_pages, int max_pages_per_seq, float scale, float* out,
+                       void* stream) {
+    if (num_segs < 0 || max_chunk_len < 0 || total_tokens < 0) return PA_EINVAL;
+    if (num_segs == 0 || max_chunk_len == 0 || total_tokens == 0) return PA_OK;
+    if (!q || !k_pages || !v_pages || !page_table || !seg_desc || !out) return PA_EINVAL;
+    int rc = check_pages(kv_dtype, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                         max_pages_per_seq);
+    if (rc != PA_OK) return rc;
+    if (num_tables < 1) return PA_EINVAL;
+    if (!isfinite(scale)) return PA_EINVAL;
+    if (num_segs > kMaxGridYZ || num_q_heads > kMaxGridYZ) return PA_EUNSUPPORTED;
+    if ((int64_t)num_tables * max_pages_per_seq > kI32Max ||
+        (int64_t)total_tokens * num_q_heads * head_dim > kI32Max * 4LL)
+        return PA_EINVAL;
+    pa::PrefillArgs a;
+    a.q = q;
+    a.k_pages = k_pages;
+    a.v_pages = v_pages;
+    a.page_table = page_table;
+    a.seg_desc = seg_desc;
+    a.out = out;
+    a.num_segs = num_segs;
+    a.num_tables = num_tables;
+    a.total_tokens = total_tokens;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.page_shift = ilog2(page_size);
+    a.num_pages = num_pages;
+    a.max_pages = max_pages_per_seq;
+    a.qscale = scale * pa::kLog2e;
+    const int q_blocks = (max_chunk_len + 15) / 16;
+    return launched(
+        pa::launch_prefill(a, kv_dtype, head_dim, q_blocks, (hipStream_t)stream));
+}
+
+int kv_page_write(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                  pa_dtype kv_dtype, const int32_t* page_table,
+                  const int32_t* token_table_index, const int32_t* token_position,
+                  int num_tokens, int num_tables, int num_kv_heads, int head_dim,
+                  int page_size, int num_pages, int max_pages_per_seq, void* stream) {
+    if (num_tokens < 0) return PA_EINVAL;
+    if (num_tokens == 0) return PA_OK;
+    if (!k_new || !v_new || !k_pages || !v_pages || !page_table || !token_table_index ||
+        !token_position)
+        return PA_EINVAL;
+    int rc = check_pages(kv_dtype, num_kv_heads, num_kv_heads, head_dim, page_size, num_pages,
+                         max_pages_per_seq);
+    if (rc != PA_OK) return rc;
+    if (num_tables < 1) return PA_EINVAL;
+    if ((int64_t)num_tables * max_pages_per_seq > kI32Max) return PA_EINVAL;
+    const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_bytes(kv_dtype);
+    if (row_bytes > kI32Max) return PA_EINVAL;
+    const int row_vec16 = (int)(row_bytes / 16);
+    if (((int64_t)num_tokens * row_vec16 + 255) / 256 > kI32Max) return PA_EINVAL;
+    pa::KvWriteArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_pages = k_pages;
+    a.v_pages = v_pages;
+    a.page_table = page_table;
+    a.token_table_index = token_table_index;
+    a.token_position = token_position;
+    a.num_tokens = num_tokens;
+    a.num_tables = num_tables;
+    a.row_vec16 = row_vec16;
+    a.page_shift = ilog2(page_size);
+    a.num_pages = num_pages;
+    a.max_pages = max_pages_per_seq;
+    return launched(pa::launch_kv_write(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// common.h — device helpers and launcher declarations shared by the gfx950 kernels.
+//
+// Element storage: K/V pages hold f32, IEEE binary16 or bfloat16 values.  Kernels move them
+// in 16-byte (128-bit) lane loads and widen to f32 in registers; all arithmetic is f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e): scores are kept in base-2 units
+constexpr float kLn2 = 0.6931471805599453f;    // ln(2): back to natural-log units on store
+
+// ---------------------------------------------------------------- cache element types
+
+struct F32 {
+    using storage = float;
+    static constexpr int kBytes = 4;
+};
+struct F16 {
+    using storage = uint16_t;
+    static constexpr int kBytes = 2;
+};
+struct BF16 {
+    using storage = uint16_t;
+    static constexpr int kBytes = 2;
+};
+
+// Widen the elements packed in one 32-bit word.
+__device__ __forceinline__ void widen_word(F32, uint32_t w, float* out) {
+    out[0] = __builtin_bit_cast(float, w);
+}
+__device__ __forceinline__ void widen_word(F16, uint32_t w, float* out) {
+    out[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    out[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ void widen_word(BF16, uint32_t w, float* out) {
+    out[0] = __builtin_bit_cast(float, w << 16);
+    out[1] = __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// Widen one 16-byte vector (4 words) into 16 / kBytes floats.
+template <typename KV>
+__device__ __forceinline__ void widen16(const uint4& v, float* out) {
+    constexpr int per = 4 / KV::kBytes;
+    widen_word(KV{}, v.x, out + 0 * per);
+    widen_word(KV{}, v.y, out + 1 * per);
+    widen_word(KV{}, v.z, out + 2 * per);
+    widen_word(KV{}, v.w, out + 3 * per);
+}
+
+// Widen one element given its raw bits (low kBytes bytes of `bits`).
+template <typename KV>
+__device__ __forceinline__ float widen1(uint32_t bits) {
+    float f[2];
+    widen_word(KV{}, bits, f);
+    return f[0];
+}
+
+// ---------------------------------------------------------------- cross-lane reductions
+
+// DPP move within 16-lane rows (the source lane always exists for these controls).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+
+constexpr int kDppQuadXor1 = 0xb1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4e;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;      // row_mirror: lane i <- lane 15-i within 16
+
+// All-reduce over aligned groups of N lanes (N a power of two, 1..64).  Every lane of a
+// group ends with the bit-identical result: each step adds the same two operands.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (N >= 2) v += dpp_mov<kDppQuadXor1>(v);
+    if constexpr (N >= 4) v += dpp_mov<kDppQuadXor2>(v);
+    if constexpr (N >= 8) v += dpp_mov<kDppHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_mov<kDppMirror>(v);
+    if constexpr (N >= 32) v += __shfl_xor(v, 16);
+    if constexpr (N >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+    if constexpr (N >= 2) v = fmaxf(v, dpp_mov<kDppQuadXor1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp_mov<kDppQuadXor2>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+    if constexpr (N >= 16) v = fmaxf(v, dpp_mov<kDppMirror>(v));
+    if constexpr (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+    if constexpr (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+
+// ---------------------------------------------------------------- launcher arguments
+
+struct DecodeArgs {
+    const float* q;
+    const void* k_pages;
+    const void* v_pages;
+    const int32_t* page_table;
+    const int32_t* context_lens;
+    float* partial_o;
+    float* partial_ml;
+    int num_seqs, num_q_heads, num_kv_heads, group, head_groups, heads_per_wg;
+    int page_shift, num_pages, max_pages, num_splits;
+    float qscale;  // scale * log2(e)
+};
+
+struct CombineArgs {
+    const float* partial_o;
+    const float* partial_ml;
+    float* out;
+    int rows;  // num_seqs * num_q_heads
+    int num_splits;
+};
+
+struct PrefillArgs {
+    const float* q;
+    const void* k_pages;
+    const void* v_pages;
+    const int32_t* page_table;
+    const int32_t* seg_desc;
+    float* out;
+    int num_segs, num_tables, total_tokens, num_q_heads, num_kv_heads, group;
+    int page_shift, num_pages, max_pages;
+    float qscale;  // scale * log2(e)
+};
+
+struct KvWriteArgs {
+    const void* k_new;
+    const void* v_new;
+    void* k_pages;
+    void* v_pages;
+    const int32_t* page_table;
+    const int32_t* token_table_index;
+    const int32_t* token_position;
+    int num_tokens, num_tables, row_vec16;  // 16-byte vectors per token row (Hkv*D*elt/16)
+    int page_shift, num_pages, max_pages;
+};
+
+// Launchers (one translation unit each).  Return the hipError_t of the launch.
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int waves,
+                         hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int q_blocks,
+                          hipStream_t stream);
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+
+}  // namespace pa

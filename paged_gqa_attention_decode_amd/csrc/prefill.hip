@@ -1,0 +1,269 @@
+// prefill.hip — causal packed prefill over segment descriptors, f32 MFMA.
+//
+// Method (crucible, "Paged attention results": descriptors {packed_start, chunk_len,
+// absolute_start, table_index}; a tile never crosses request ownership; a packed row at
+// absolute P reads only its own request's positions 0..P; every logical page a tile crosses
+// is translated separately.  The online softmax of the same page: m' = max(m, tile max),
+// rescale by exp(m - m'), accumulate exp(score - m') and its weighted V, divide after the
+// last visible tile.  crucible README scheduler section: chunk row r attends 0 ..= done + r).
+//
+// gfx950 mapping
+//   grid  (ceil(max_chunk_len / 16), Hq, num_segs); 4 waves per workgroup, all on the same
+//         16 query rows of one head.  The causal key range of the block is cut into 32-key
+//         tiles dealt round-robin to the 4 waves, so a long history is shared by 4 SIMDs;
+//         the 4 partial softmax states merge through LDS at the end.
+//   math  v_mfma_f32_16x16x4_f32.  Scores are computed transposed, S^T = K * Q^T (16 keys x
+//         16 rows per MFMA), so each lane ends with 4 keys of ONE query row (row = lane % 16).
+//         That register layout is exactly the B operand P^T of O^T += V^T * P^T, so the
+//         probabilities never leave registers, and the O^T accumulator also keeps one query
+//         row per lane: row max, rescale and sum stay lane-local except for one max over the
+//         4 lane groups per tile.
+//   data  K rows are read 4 consecutive dims per lane (16 B for f32); V is read one element
+//         per lane, 16 consecutive dims per 16 lanes.  Keys past the block's last visible
+//         position are neither loaded nor counted; keys past a row's own position are
+//         masked to -inf before the exponential.  Q is pre-scaled by scale*log2(e).
+#include "common.h"
+
+namespace pa {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Four consecutive elements starting at p, widened to f32.
+template <typename KV>
+__device__ __forceinline__ void load4(const typename KV::storage* p, float* out) {
+    if constexpr (KV::kBytes == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(p);
+        out[0] = t.x;
+        out[1] = t.y;
+        out[2] = t.z;
+        out[3] = t.w;
+    } else {
+        const uint2 t = *reinterpret_cast<const uint2*>(p);
+        widen_word(KV{}, t.x, out);
+        widen_word(KV{}, t.y, out + 2);
+    }
+}
+
+template <typename KV>
+__device__ __forceinline__ float load1(const typename KV::storage* p) {
+    if constexpr (KV::kBytes == 4) {
+        return *p;
+    } else {
+        return widen1<KV>((uint32_t)*p);
+    }
+}
+
+constexpr int kWaves = 4;
+constexpr int kRows = 16;     // query rows per workgroup
+constexpr int kTileKeys = 32; // keys per wave per step (two 16-key MFMA blocks)
+
+template <typename KV, int D>
+__global__ void __launch_bounds__(kWaves * 64) prefill_kernel(PrefillArgs a) {
+    using T = typename KV::storage;
+    constexpr int NC = D / 16;  // 16-wide dimension blocks
+
+    __shared__ float s_m[kWaves][kRows];
+    __shared__ float s_l[kWaves][kRows];
+    __shared__ float s_o[kWaves][D][kRows];
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;    // MFMA k-group: 4 lane groups of 16
+    const int c16 = lane & 15;  // query row within the block (B/D operand column)
+
+    const int32_t* dsc = a.seg_desc + 4 * (size_t)blockIdx.z;
+    const int start = dsc[0];
+    int len = dsc[1];
+    const int a0 = dsc[2];
+    const int ti = dsc[3];
+    const int cap = a.max_pages << a.page_shift;
+    if (start < 0 || start >= a.total_tokens || len <= 0 || a0 < 0 || a0 >= cap || ti < 0 ||
+        ti >= a.num_tables)
+        return;
+    len = min(min(len, a.total_tokens - start), cap - a0);
+    const int r0 = blockIdx.x * kRows;
+    if (r0 >= len) return;
+
+    const int h = blockIdx.y;
+    const int kvh = h / a.group;
+    const int kmax = a0 + min(r0 + kRows - 1, len - 1);  // last key any row here may see
+    const int r = r0 + c16;
+    const bool rvalid = r < len;
+    const int qend = a0 + r;  // this lane's row sees keys 0..qend
+
+    // Q^T operand: lane (g, c16) holds Q[row][16c + 4g + kk], kk = 0..3.
+    float qr[NC][4];
+    {
+        const float* qp =
+            a.q + ((size_t)(start + min(r, len - 1)) * a.num_q_heads + h) * D + 4 * g;
+        const float qs = rvalid ? a.qscale : 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float4 t = *reinterpret_cast<const float4*>(qp + 16 * c);
+            qr[c][0] = t.x * qs;
+            qr[c][1] = t.y * qs;
+            qr[c][2] = t.z * qs;
+            qr[c][3] = t.w * qs;
+        }
+    }
+
+    const int32_t* trow = a.page_table + (size_t)ti * a.max_pages;
+    const T* kp = reinterpret_cast<const T*>(a.k_pages) + (size_t)kvh * D;
+    const T* vp = reinterpret_cast<const T*>(a.v_pages) + (size_t)kvh * D;
+    const size_t slot_stride = (size_t)a.num_kv_heads * D;
+    const int pshift = a.page_shift;
+    const int pmask = (1 << pshift) - 1;
+    auto row_off = [&](int key) -> size_t {
+        const int page = clampi(trow[min(key >> pshift, a.max_pages - 1)], 0, a.num_pages - 1);
+        return (((size_t)page << pshift) | (size_t)(key & pmask)) * slot_stride;
+    };
+
+    float m = -INFINITY;
+    float lsum = 0.f;
+    floatx4 oacc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) oacc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int ntiles = (kmax + kTileKeys) / kTileKeys;
+    for (int t = wave; t < ntiles; t += kWaves) {
+        const int j0 = t * kTileKeys;
+        // K operand: lane (g, c16) of block st holds K[j0 + 16 st + c16][16c + 4g + kk].
+        float kf[2][NC][4];
+        // V^T operand of MFMA (st, i): lane (g, c16) holds V[j0 + 16 st + 4g + i][16dt + c16].
+        float vf[2][4][NC];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const int key = j0 + 16 * st + c16;
+            if (key <= kmax) {
+                const T* kr = kp + row_off(key) + 4 * g;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) load4<KV>(kr + 16 * c, kf[st][c]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) kf[st][c][kk] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int vkey = j0 + 16 * st + 4 * g + i;
+                if (vkey <= kmax) {
+                    const T* vr = vp + row_off(vkey) + c16;
+#pragma unroll
+                    for (int dt = 0; dt < NC; ++dt) vf[st][i][dt] = load1<KV>(vr + 16 * dt);
+                } else {
+#pragma unroll
+                    for (int dt = 0; dt < NC; ++dt) vf[st][i][dt] = 0.f;
+                }
+            }
+        }
+
+        // S^T = K Q^T: lane (g, c16) gets scores of keys j0 + 16 st + 4g + i for row c16.
+        floatx4 sacc[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            sacc[st] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) sacc[st] = mfma16(kf[st][c][kk], qr[c][kk], sacc[st]);
+        }
+
+        float tmax = -INFINITY;
+        float s[2][4];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = j0 + 16 * st + 4 * g + i;
+                s[st][i] = (rvalid && key <= qend) ? sacc[st][i] : -INFINITY;
+                tmax = fmaxf(tmax, s[st][i]);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mn = fmaxf(m, tmax);
+        const float ms = (mn == -INFINITY) ? 0.f : mn;
+        const float alpha = fast_exp2(m - ms);
+        float p[2][4];
+        float ps = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[st][i] = fast_exp2(s[st][i] - ms);
+                ps += p[st][i];
+            }
+        lsum = fmaf(lsum, alpha, ps);
+        m = mn;
+#pragma unroll
+        for (int dt = 0; dt < NC; ++dt) oacc[dt] *= alpha;
+
+        // O^T += V^T P^T.
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int dt = 0; dt < NC; ++dt) oacc[dt] = mfma16(vf[st][i][dt], p[st][i], oacc[dt]);
+    }
+
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (g == 0) {
+        s_m[wave][c16] = m;
+        s_l[wave][c16] = lsum;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NC; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_o[wave][16 * dt + 4 * g + i][c16] = oacc[dt][i];
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < kRows * D; idx += kWaves * 64) {
+        const int q = idx / D;
+        const int d = idx - q * D;
+        if (r0 + q >= len) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][q]);
+        const float ms = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = fast_exp2(s_m[w][q] - ms);
+            L = fmaf(s_l[w][q], f, L);
+            O = fmaf(s_o[w][d][q], f, O);
+        }
+        a.out[((size_t)(start + r0 + q) * a.num_q_heads + h) * D + d] = (L > 0.f) ? O / L : 0.f;
+    }
+}
+
+template <typename KV, int D>
+hipError_t launch_typed(const PrefillArgs& a, int q_blocks, hipStream_t stream) {
+    const dim3 grid(q_blocks, a.num_q_heads, a.num_segs);
+    hipLaunchKernelGGL((prefill_kernel<KV, D>), grid, dim3(kWaves * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int q_blocks,
+                          hipStream_t stream) {
+    (void)q_blocks;
+    const int qb = q_blocks;
+    if (head_dim == 64) {
+        if (kv_dtype == 0) return launch_typed<F32, 64>(a, qb, stream);
+        if (kv_dtype == 1) return launch_typed<F16, 64>(a, qb, stream);
+        return launch_typed<BF16, 64>(a, qb, stream);
+    }
+    if (kv_dtype == 0) return launch_typed<F32, 128>(a, qb, stream);
+    if (kv_dtype == 1) return launch_typed<F16, 128>(a, qb, stream);
+    return launch_typed<BF16, 128>(a, qb, stream);
+}
+
+}  // namespace pa

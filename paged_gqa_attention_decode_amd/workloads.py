@@ -186,7 +186,10 @@ def make_decode_case(rng: np.random.Generator, *, batch, hq, hkv, head_dim, page
     if max_pages_per_seq == 0:
         max_pages_per_seq = max(1, -(-max_ctx // page_size))
     if num_pages == 0:
-        num_pages = rotations * batch * max_pages_per_seq
+        if drawn_ctx:
+            num_pages = rotations * batch * max_pages_per_seq
+        else:   # exactly the pages the sequences need, plus two spare (poisoned) pages
+            num_pages = rotations * sum(-(-int(c) // page_size) for c in ctx_arr) + 2
     shape = (num_pages, page_size, hkv, head_dim)
     k_pages = _normal_pool(rng, shape, dtype)
     v_pages = _normal_pool(rng, shape, dtype)

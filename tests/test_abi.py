@@ -1,0 +1,174 @@
+"""CPU: the C-ABI library loads, exports every function include/paged_attn.h declares, and
+its host-side validation rejects malformed calls before anything reaches the device.
+
+Every call here either carries an invalid argument or is an empty call; none can launch."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_gqa_attention_decode_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: each call fails validation first
+NULL = ctypes.c_void_p(0)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_lists_the_four_entry_points():
+    names = header_functions()
+    for n in ("paged_attn_decode", "paged_attn_combine", "paged_attn_prefill",
+              "kv_page_write", "paged_attn_decode_workspace_bytes",
+              "paged_attn_status_string"):
+        assert n in names
+    assert set(names) == set(pa.C_FUNCTIONS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in header_functions() if n not in exported]
+    assert not missing, missing
+    lib = pa.raw_library()
+    for n in header_functions():
+        assert hasattr(lib, n)
+
+
+def test_status_strings():
+    assert pa.paged_attn_status_string(0) == "ok"
+    assert pa.paged_attn_status_string(-1) == "invalid argument"
+    assert pa.paged_attn_status_string(-2) == "unsupported configuration"
+    assert pa.paged_attn_status_string(-3) == "kernel launch failed"
+    assert pa.paged_attn_status_string(42) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert pa.paged_attn_decode_workspace_bytes(1, 40, 128, 32) == 40 * 32 * 130 * 4
+    assert pa.paged_attn_decode_workspace_bytes(16, 64, 128, 16) == 16 * 64 * 16 * 130 * 4
+    assert pa.paged_attn_decode_workspace_bytes(0, 40, 128, 32) == 0
+    assert pa.paged_attn_decode_workspace_bytes(1, 40, 128, 0) == 0
+
+
+# decode(q, k, v, dtype, table, ctx, B, Hq, Hkv, D, ps, P, maxp, scale, S, po, pml, stream)
+GOOD_DECODE = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, table=FAKE, ctx=FAKE, B=1, Hq=40, Hkv=8,
+                   D=128, ps=16, P=204, maxp=204, scale=0.0884, S=32, po=FAKE, pml=FAKE)
+
+
+def decode(**kw):
+    a = dict(GOOD_DECODE, **kw)
+    return pa.raw_library().paged_attn_decode(
+        a["q"], a["k"], a["v"], a["dtype"], a["table"], a["ctx"], a["B"], a["Hq"], a["Hkv"],
+        a["D"], a["ps"], a["P"], a["maxp"], a["scale"], a["S"], a["po"], a["pml"], NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0, q=NULL), pa.PA_OK),                  # empty batch: valid, nothing enqueued
+    (dict(B=-1), pa.PA_EINVAL),
+    (dict(q=NULL), pa.PA_EINVAL),
+    (dict(k=NULL), pa.PA_EINVAL),
+    (dict(po=NULL), pa.PA_EINVAL),
+    (dict(pml=NULL), pa.PA_EINVAL),
+    (dict(table=NULL), pa.PA_EINVAL),
+    (dict(ctx=NULL), pa.PA_EINVAL),
+    (dict(Hq=41, q=NULL), pa.PA_EINVAL),            # Hq not a multiple of Hkv
+    (dict(Hq=41), pa.PA_EINVAL),
+    (dict(Hkv=0), pa.PA_EINVAL),
+    (dict(D=96), pa.PA_EUNSUPPORTED),
+    (dict(D=0), pa.PA_EINVAL),
+    (dict(ps=12), pa.PA_EUNSUPPORTED),
+    (dict(ps=0), pa.PA_EINVAL),
+    (dict(ps=8192), pa.PA_EUNSUPPORTED),
+    (dict(S=0), pa.PA_EINVAL),
+    (dict(S=5000), pa.PA_EUNSUPPORTED),
+    (dict(dtype=7), pa.PA_EINVAL),
+    (dict(Hq=65 * 8), pa.PA_EUNSUPPORTED),          # group of 65 query heads
+    (dict(scale=math.nan), pa.PA_EINVAL),
+    (dict(scale=math.inf), pa.PA_EINVAL),
+    (dict(maxp=2 ** 28, ps=16), pa.PA_EINVAL),      # capacity overflows int32
+    (dict(P=0), pa.PA_EINVAL),
+    (dict(B=70000), pa.PA_EUNSUPPORTED),
+])
+def test_decode_validation(kw, status):
+    assert decode(**kw) == status
+
+
+def test_combine_validation():
+    c = pa.raw_library().paged_attn_combine
+    assert c(FAKE, FAKE, 0, 40, 128, 32, FAKE, NULL) == pa.PA_OK
+    assert c(NULL, FAKE, 1, 40, 128, 32, FAKE, NULL) == pa.PA_EINVAL
+    assert c(FAKE, FAKE, 1, 40, 128, 32, NULL, NULL) == pa.PA_EINVAL
+    assert c(FAKE, FAKE, 1, 40, 96, 32, FAKE, NULL) == pa.PA_EUNSUPPORTED
+    assert c(FAKE, FAKE, 1, 40, 128, 0, FAKE, NULL) == pa.PA_EINVAL
+    assert c(FAKE, FAKE, 1, 0, 128, 32, FAKE, NULL) == pa.PA_EINVAL
+    assert c(FAKE, FAKE, -1, 40, 128, 32, FAKE, NULL) == pa.PA_EINVAL
+
+
+def test_prefill_validation():
+    p = pa.raw_library().paged_attn_prefill
+    # (q, k, v, dtype, table, desc, nseg, ntab, T, maxchunk, Hq, Hkv, D, ps, P, maxp, scale,
+    #  out, stream)
+    good = [FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1, 1, 512, 512, 12, 12, 64, 16, 32, 32, 0.125,
+            FAKE, NULL]
+
+    def call(over):
+        args = list(good)
+        for k, v in over.items():
+            args[k] = v
+        return p(*args)
+
+    assert call({6: 0}) == pa.PA_OK                     # no segments
+    assert call({9: 0, 0: NULL}) == pa.PA_OK            # max_chunk_len 0
+    assert call({0: NULL}) == pa.PA_EINVAL
+    assert call({5: NULL}) == pa.PA_EINVAL
+    assert call({17: NULL}) == pa.PA_EINVAL
+    assert call({7: 0}) == pa.PA_EINVAL                 # no page tables
+    assert call({6: -1}) == pa.PA_EINVAL
+    assert call({10: 13}) == pa.PA_EINVAL               # 13 % 12
+    assert call({12: 80}) == pa.PA_EUNSUPPORTED
+    assert call({13: 24}) == pa.PA_EUNSUPPORTED
+    assert call({3: 3}) == pa.PA_EINVAL
+    assert call({16: math.nan}) == pa.PA_EINVAL
+    assert call({6: 70000}) == pa.PA_EUNSUPPORTED
+
+
+def test_kv_write_validation():
+    w = pa.raw_library().kv_page_write
+    # (k_new, v_new, k_pages, v_pages, dtype, table, owner, pos, T, ntab, Hkv, D, ps, P,
+    #  maxp, stream)
+    good = [FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, 16, 16, 8, 128, 32, 8192, 128, NULL]
+
+    def call(over):
+        args = list(good)
+        for k, v in over.items():
+            args[k] = v
+        return w(*args)
+
+    assert call({8: 0, 0: NULL}) == pa.PA_OK            # no tokens
+    assert call({8: -1}) == pa.PA_EINVAL
+    for i in (0, 1, 2, 3, 5, 6, 7):
+        assert call({i: NULL}) == pa.PA_EINVAL, i
+    assert call({9: 0}) == pa.PA_EINVAL
+    assert call({11: 256}) == pa.PA_EUNSUPPORTED
+    assert call({12: 48}) == pa.PA_EUNSUPPORTED
+    assert call({4: -1}) == pa.PA_EINVAL
+    assert call({10: 0}) == pa.PA_EINVAL
+
+
+def test_python_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 8, 64)
+    k = torch.zeros(16, 16, 2, 64)
+    with pytest.raises(ValueError, match="device"):
+        pa.paged_attn_decode(q, k, k, torch.zeros(1, 16, dtype=torch.int32),
+                             torch.ones(1, dtype=torch.int32), 0.125,
+                             torch.zeros(1, 8, 4, 64), torch.zeros(1, 8, 4, 2))

@@ -1,0 +1,158 @@
+"""GPU: bit-exact invariants of the HIP path itself.
+
+* context length 1 returns V[0] exactly (exp(0) = 1, sum 1);
+* relabelling physical pages changes no bit (paging moves storage, not arithmetic —
+  crucible README, "Paged KV cache and continuous batching", Correctness);
+* a sequence's output does not depend on its batch companions or their order
+  (crucible README, gpu-batch check);
+* GQA equals MHA with K/V repeated per group (crucible README, "Tests");
+* repeated runs are bit-identical; poisoned never-read bytes never reach an output;
+* a prefill segment's rows do not depend on the other segments packed with it."""
+import numpy as np
+import pytest
+import torch
+
+import paged_gqa_attention_decode_amd as pa
+from compare import assert_bitwise
+from gpu_helpers import DEV, DecodeRun, announce, dev, host
+from paged_gqa_attention_decode_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def f32_values(bits, dtype):
+    """Stored cache values as float32 (library conversions; exact for f16 and bf16)."""
+    if dtype == "f32":
+        return np.asarray(bits, np.float32)
+    if dtype == "f16":
+        return np.asarray(bits, np.uint16).view(np.float16).astype(np.float32)
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,S", [("f32", 8, 2, 64, 16), ("f16", 40, 8, 128, 32),
+                                               ("bf16", 64, 8, 128, 1), ("bf16", 12, 1, 64, 3)])
+def test_ctx1_returns_v0_exactly(dtype, hq, hkv, d, S):
+    announce(f"ctx=1 exact {dtype} {hq}/{hkv} d={d} S={S}")
+    rng = wl.rng_for([600, hq, d])
+    case = wl.make_decode_case(rng, batch=3, hq=hq, hkv=hkv, head_dim=d, page_size=16,
+                               dtype=dtype, ctx=[1, 1, 1], num_splits=S)
+    out = DecodeRun(case).step()
+    expect = np.repeat(f32_values(case.v_new, dtype), hq // hkv, axis=1)
+    assert_bitwise(out, expect, "ctx=1")
+
+
+def _decode(case, S=None, table=None, kp=None, vp=None):
+    run = DecodeRun(case, num_splits=S)
+    if table is not None:
+        run.table = dev(table)
+        run.kp = dev(kp, case.dtype)
+        run.vp = dev(vp, case.dtype)
+    out = run.step()
+    return out, host(run.po), host(run.pml)
+
+
+def test_page_permutation_bitwise():
+    announce("page permutation bitwise")
+    rng = wl.rng_for(601)
+    case = wl.make_decode_case(rng, batch=4, hq=40, hkv=8, head_dim=128, page_size=16,
+                               dtype="f16", ctx=[3254, 17, 1000, 129], num_splits=32)
+    base = _decode(case)
+    pi = rng.permutation(case.k_pages.shape[0])
+    kp2 = np.empty_like(case.k_pages)
+    vp2 = np.empty_like(case.v_pages)
+    kp2[pi] = case.k_pages
+    vp2[pi] = case.v_pages
+    table2 = np.where(case.page_table >= 0, pi[np.maximum(case.page_table, 0)], -1)
+    other = _decode(case, table=table2.astype(np.int32), kp=kp2, vp=vp2)
+    for a, b, name in zip(base, other, ("out", "partial_o", "partial_ml")):
+        assert_bitwise(a, b, f"page permutation {name}")
+
+
+def test_batch_composition_bitwise():
+    announce("batch composition bitwise")
+    rng = wl.rng_for(602)
+    case = wl.make_decode_case(rng, batch=5, hq=64, hkv=8, head_dim=128, page_size=32,
+                               dtype="bf16", ctx=[4096, 64, 1, 2000, 333], num_splits=16)
+    full = _decode(case)[0]
+    for b in range(5):
+        sub = wl.DecodeCase(
+            q=case.q[b:b + 1], k_pages=case.k_pages, v_pages=case.v_pages,
+            page_table=case.page_table[b:b + 1], context_lens=case.context_lens[b:b + 1],
+            k_new=case.k_new[b:b + 1], v_new=case.v_new[b:b + 1],
+            token_table_index=np.zeros(1, np.int32), token_position=case.token_position[b:b + 1],
+            dtype=case.dtype, scale=case.scale, num_splits=case.num_splits)
+        assert_bitwise(_decode(sub)[0][0], full[b], f"sequence {b} alone vs batched")
+    order = np.arange(5)[::-1].copy()
+    rev = wl.DecodeCase(
+        q=case.q[order], k_pages=case.k_pages, v_pages=case.v_pages,
+        page_table=case.page_table[order], context_lens=case.context_lens[order],
+        k_new=case.k_new[order], v_new=case.v_new[order],
+        token_table_index=np.arange(5, dtype=np.int32), token_position=case.token_position[order],
+        dtype=case.dtype, scale=case.scale, num_splits=case.num_splits)
+    assert_bitwise(_decode(rev)[0][order], full, "reversed batch order")
+
+
+@pytest.mark.parametrize("g", [4, 5, 7, 8, 12])
+def test_gqa_equals_repeated_kv_mha_bitwise(g):
+    announce(f"GQA g={g} vs MHA bitwise")
+    rng = wl.rng_for([603, g])
+    hkv = 2
+    case = wl.make_decode_case(rng, batch=2, hq=hkv * g, hkv=hkv, head_dim=128, page_size=16,
+                               dtype="f16", ctx=[700, 1641], num_splits=16)
+    gqa = _decode(case)[0]
+    mha = wl.DecodeCase(
+        q=case.q, k_pages=np.repeat(case.k_pages, g, axis=2),
+        v_pages=np.repeat(case.v_pages, g, axis=2), page_table=case.page_table,
+        context_lens=case.context_lens, k_new=np.repeat(case.k_new, g, axis=1),
+        v_new=np.repeat(case.v_new, g, axis=1), token_table_index=case.token_table_index,
+        token_position=case.token_position, dtype=case.dtype, scale=case.scale,
+        num_splits=case.num_splits)
+    assert_bitwise(_decode(mha)[0], gqa, f"GQA g={g} vs MHA")
+
+
+def test_repeat_runs_bitwise_and_poison_stays_out():
+    announce("determinism + poison")
+    w = wl.WORKLOADS["decode_hq28_hkv4_d128_ctx1641_f16"]
+    case = wl.workload_decode_case(w)
+    a = _decode(case)
+    b = _decode(case)
+    for x, y, name in zip(a, b, ("out", "partial_o", "partial_ml")):
+        assert_bitwise(x, y, f"repeat {name}")
+    assert np.isfinite(a[0]).all() and np.isfinite(a[1]).all()
+
+
+def test_prefill_segment_isolation_bitwise():
+    """A segment's rows are identical whether it is prefilled alone or packed with others,
+    and whatever its physical pages are."""
+    announce("prefill segment isolation")
+    rng = wl.rng_for(604)
+    case = wl.make_prefill_case(rng, hq=12, hkv=3, head_dim=64, page_size=16, dtype="f32",
+                                lens=[17, 64, 129, 257], starts=[0, 63, 255, 512])
+
+    def run(c):
+        kp, vp = dev(c.k_pages, c.dtype), dev(c.v_pages, c.dtype)
+        table = dev(c.page_table)
+        pa.kv_page_write(dev(c.k_new, c.dtype), dev(c.v_new, c.dtype), kp, vp, table,
+                         dev(c.token_table_index), dev(c.token_position))
+        out = torch.zeros(c.q.shape, device=DEV)
+        pa.paged_attn_prefill(dev(c.q), kp, vp, table, dev(c.seg_desc), c.max_chunk_len,
+                              c.scale, out)
+        torch.cuda.synchronize()
+        return host(out)
+
+    full = run(case)
+    assert np.isfinite(full).all()
+    for i in range(4):
+        start, n = int(case.seg_desc[i, 0]), int(case.seg_desc[i, 1])
+        rows = slice(start, start + n)
+        desc = case.seg_desc[i:i + 1].copy()
+        desc[0, 0] = 0
+        alone = wl.PrefillCase(
+            q=case.q[rows], k_pages=case.k_pages, v_pages=case.v_pages,
+            page_table=case.page_table, seg_desc=desc, k_new=case.k_new[rows],
+            v_new=case.v_new[rows], token_table_index=case.token_table_index[rows],
+            token_position=case.token_position[rows], dtype=case.dtype, scale=case.scale)
+        assert_bitwise(run(alone), full[rows], f"segment {i} alone vs packed")

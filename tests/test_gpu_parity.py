@@ -1,0 +1,257 @@
+"""GPU: the HIP path against the f64 oracle, element by element, on seeded inputs.
+
+Bars: page writes bit-exact; decode and prefill outputs within max-abs 1e-5 for f32 K/V and
+|gpu - ref| <= 2e-3 + 1e-2 |ref| for f16/bf16 K/V.  Split partials are compared as
+(m, l, O/l) against the oracle's partials under the same partition rule."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_gqa_attention_decode_amd as pa
+from compare import assert_bitwise, assert_within, tolerance
+from gpu_helpers import DEV, DecodeRun, announce, dev, host
+from paged_gqa_attention_decode_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def oracle_step(case):
+    """Oracle: page write of the current token, then attention over the whole context."""
+    kp, vp = oracle.kv_write(case.k_new, case.v_new, case.k_pages, case.v_pages, case.dtype,
+                             case.page_table, case.token_table_index, case.token_position)
+    out = oracle.decode(case.q, kp, vp, case.dtype, case.page_table, case.context_lens,
+                        case.scale)
+    return kp, vp, out
+
+
+def check_partials(run, case, kp, vp):
+    po = host(run.po).astype(np.float64)
+    pml = host(run.pml).astype(np.float64)
+    ro, rm, rl = oracle.decode_partials(case.q, kp, vp, case.dtype, case.page_table,
+                                        case.context_lens, case.scale, run.S)
+    m, l = pml[..., 0], pml[..., 1]
+    idle = rl == 0
+    assert np.array_equal(l == 0, idle), "idle-split pattern differs"
+    assert np.all(m[idle] == -np.inf) and np.all(po[idle] == 0.0)
+    live = ~idle
+    assert_within(m[live], rm[live], 1e-4, 1e-6, "split max m")
+    assert_within(l[live], rl[live], 0.0, 2e-4, "split sum l")
+    atol, rtol = tolerance(case.dtype)
+    assert_within(po[live] / l[live][:, None], ro[live] / rl[live][:, None], atol, rtol,
+                  "split O/l")
+
+
+# ----------------------------------------------------------------------------- page write
+
+@pytest.mark.parametrize("dtype,ps,hkv,d", [("f32", 16, 12, 64), ("f16", 16, 8, 128),
+                                             ("bf16", 32, 8, 128), ("f32", 1, 2, 128),
+                                             ("bf16", 4096, 1, 64)])
+def test_kv_page_write_bit_exact(dtype, ps, hkv, d):
+    announce(f"kv_page_write {dtype} ps={ps} hkv={hkv} d={d}")
+    rng = wl.rng_for([200, ps, hkv, d])
+    num_pages, max_pages, ntab = 14, 4, 3
+    kp = np.full((num_pages, ps, hkv, d), wl.nan_value(dtype), wl.storage_dtype(dtype))
+    vp = kp.copy()
+    table = rng.permutation(num_pages)[: ntab * max_pages].reshape(ntab, max_pages)
+    table = table.astype(np.int32)
+    table[2, 3] = 99                                          # out-of-range page id
+    T = 40
+    owner = rng.integers(-1, ntab + 1, size=T).astype(np.int32)  # includes -1 and ntab
+    cap = max_pages * ps
+    pos = rng.integers(0, cap + 2, size=T).astype(np.int32)       # includes cap, cap+1
+    # unique (owner, pos) pairs so no two tokens race for one slot
+    _, first = np.unique(owner.astype(np.int64) * (cap + 8) + pos, return_index=True)
+    keep = np.sort(first)
+    owner, pos = owner[keep], pos[keep]
+    k_new = wl.to_storage(rng.standard_normal((owner.size, hkv, d)).astype(np.float32), dtype)
+    v_new = wl.to_storage(rng.standard_normal((owner.size, hkv, d)).astype(np.float32), dtype)
+    rk, rv = oracle.kv_write(k_new, v_new, kp, vp, dtype, table, owner, pos)
+    gk, gv = dev(kp, dtype), dev(vp, dtype)
+    pa.kv_page_write(dev(k_new, dtype), dev(v_new, dtype), gk, gv, dev(table), dev(owner),
+                     dev(pos))
+    torch.cuda.synchronize()
+    assert_bitwise(host(gk), rk, "K pool")
+    assert_bitwise(host(gv), rv, "V pool")
+
+
+# ----------------------------------------------------------------------------- named decode
+
+DECODE_WORKLOADS = [n for n, w in wl.WORKLOADS.items() if w.kind == "decode"]
+
+
+@pytest.mark.parametrize("name", DECODE_WORKLOADS)
+def test_decode_workload(name):
+    """Full-size parity of every named decode workload, in the bench's launch configuration
+    (write of the current token -> split decode with the workload's split count -> combine)."""
+    w = wl.WORKLOADS[name]
+    case = wl.workload_decode_case(w)
+    announce(f"decode workload {name} S={case.num_splits} ctx={case.context_lens.tolist()}")
+    run = DecodeRun(case)
+    out = run.step()
+    kp, vp, ref = oracle_step(case)
+    assert_bitwise(host(run.kp), kp, "K pool after write")
+    atol, rtol = tolerance(case.dtype)
+    assert_within(out, ref, atol, rtol, f"decode {name}")
+    check_partials(run, case, kp, vp)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 16, 64, 4096])
+def test_decode_split_counts(splits):
+    w = wl.WORKLOADS["decode_hq40_hkv8_d128_ctx3254_f16"]
+    case = wl.workload_decode_case(w)
+    announce(f"decode 14B shape S={splits}")
+    run = DecodeRun(case, num_splits=splits)
+    out = run.step()
+    kp, vp, ref = oracle_step(case)
+    assert_within(out, ref, *tolerance("f16"), f"decode S={splits}")
+    check_partials(run, case, kp, vp)
+
+
+BOUNDARY_CTX = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257,
+                511, 512, 685, 941, 1000, 1023, 1024, 1919, 1920, 1921, 2807, 2808, 3254,
+                4095, 4096]
+
+
+@pytest.mark.parametrize("geom", [(40, 8, 128, 16, "f16", 32), (28, 4, 128, 16, "f16", 32),
+                                  (64, 8, 128, 32, "bf16", 16), (8, 2, 64, 16, "f32", 16),
+                                  (12, 3, 64, 16, "f32", 8), (16, 16, 128, 32, "bf16", 4),
+                                  (32, 2, 64, 16, "bf16", 8), (12, 1, 128, 16, "f16", 16)],
+                         ids=lambda g: "hq{}_hkv{}_d{}_ps{}_{}_S{}".format(*g))
+def test_decode_boundary_lengths(geom):
+    """Every boundary length of the pages' fixture lists in one batch."""
+    hq, hkv, d, ps, dtype, S = geom
+    announce(f"decode boundary lengths {geom}")
+    rng = wl.rng_for([300, hq, hkv, d, ps])
+    case = wl.make_decode_case(rng, batch=len(BOUNDARY_CTX), hq=hq, hkv=hkv, head_dim=d,
+                               page_size=ps, dtype=dtype, ctx=BOUNDARY_CTX, num_splits=S)
+    run = DecodeRun(case)
+    out = run.step()
+    kp, vp, ref = oracle_step(case)
+    assert_within(out, ref, *tolerance(dtype), f"decode boundary {geom}")
+    check_partials(run, case, kp, vp)
+
+
+def test_decode_table_longer_than_lds_stage():
+    """Page size 1 with 3000 tokens: the table row exceeds one LDS stage (1024 entries)."""
+    announce("decode ps=1 ctx=3000 (segmented table staging)")
+    rng = wl.rng_for(301)
+    case = wl.make_decode_case(rng, batch=2, hq=8, hkv=2, head_dim=64, page_size=1,
+                               dtype="bf16", ctx=[3000, 1500], num_splits=2)
+    run = DecodeRun(case)
+    out = run.step()
+    _, _, ref = oracle_step(case)
+    assert_within(out, ref, *tolerance("bf16"), "decode ps=1")
+
+
+def test_decode_outlier_data():
+    """The minfer D3-6 outlier generators (|q| ~ 57, |v| ~ 144) on the 14B geometry."""
+    announce("decode outlier data")
+    hq, hkv, d, n = 40, 8, 128, 1921
+    rng = wl.rng_for(302)
+    case = wl.make_decode_case(rng, batch=1, hq=hq, hkv=hkv, head_dim=d, page_size=16,
+                               dtype="f16", ctx=[n], num_splits=32, new_token_in_pool=True)
+    case.q[:] = np.array([(((i * 37) % 19) / 5.0 - 1.9) * 30.0 for i in range(hq * d)],
+                         np.float32).reshape(1, hq, d)
+    vals = np.array([(((i * 57) % 11) / 3.0 - 1.8) * 80.0 for i in range(n * hkv * d)],
+                    np.float32).reshape(n, hkv, d)
+    for t in range(n):
+        p = case.page_table[0, t // 16]
+        case.v_pages[p, t % 16] = wl.to_storage(vals[t], "f16")
+    case.v_new[0] = case.v_pages[case.page_table[0, (n - 1) // 16], (n - 1) % 16]
+    run = DecodeRun(case)
+    out = run.step()
+    _, _, ref = oracle_step(case)
+    assert_within(out, ref, *tolerance("f16"), "decode outliers")
+
+
+# ----------------------------------------------------------------------------- combine alone
+
+@pytest.mark.parametrize("d,S", [(64, 1), (64, 16), (128, 32), (128, 33), (128, 4096)])
+def test_combine_synthetic_partials(d, S):
+    announce(f"combine d={d} S={S}")
+    rng = wl.rng_for([400, d, S])
+    B = 1 if S > 1024 else 3
+    o, ml = wl.make_partials(rng, batch=B, hq=40, head_dim=d, num_splits=S, all_empty_rows=2)
+    ref = oracle.combine(o, ml[..., 0], ml[..., 1])
+    out = torch.full((B, 40, d), float("nan"), device=DEV)
+    pa.paged_attn_combine(dev(o), dev(ml), out)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.all(got.reshape(-1, d)[:2] == 0.0), "all-idle rows must be zero"
+    # f32 sums over S splits: besides the 1e-5 floor, allow the summation bound
+    # 2 * S * 2^-24 * (sum_s w_s |O_s|) / (sum_s w_s l_s), w_s = exp(m_s - M), in f64.
+    m64, l64, o64 = ml[..., 0].astype(np.float64), ml[..., 1].astype(np.float64), o
+    M = np.max(np.where(l64 > 0, m64, -np.inf), axis=-1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        w = np.where(l64 > 0, np.exp(m64 - M), 0.0)
+        bound = (w[..., None] * np.abs(o64)).sum(-2) / np.maximum((w * l64).sum(-1), 1e-30)[..., None]
+    tol = 1e-5 + 2.0 * S * 2.0 ** -24 * np.nan_to_num(bound)
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), f"combine d={d} S={S}: max err/tol {np.max(err / tol):.3f}"
+
+
+# ----------------------------------------------------------------------------- prefill
+
+def run_prefill(case, out_fill=np.nan):
+    dt = case.dtype
+    kp, vp = dev(case.k_pages, dt), dev(case.v_pages, dt)
+    table = dev(case.page_table)
+    pa.kv_page_write(dev(case.k_new, dt), dev(case.v_new, dt), kp, vp, table,
+                     dev(case.token_table_index), dev(case.token_position))
+    out = torch.full(case.q.shape, float(out_fill), device=DEV)
+    pa.paged_attn_prefill(dev(case.q), kp, vp, table, dev(case.seg_desc), case.max_chunk_len,
+                          case.scale, out)
+    torch.cuda.synchronize()
+    return host(out), host(kp), host(vp)
+
+
+def oracle_prefill(case):
+    kp, vp = oracle.kv_write(case.k_new, case.v_new, case.k_pages, case.v_pages, case.dtype,
+                             case.page_table, case.token_table_index, case.token_position)
+    out, count = oracle.prefill(case.q, kp, vp, case.dtype, case.page_table, case.seg_desc,
+                                case.scale)
+    return out, kp, vp, count
+
+
+def test_prefill_workload():
+    w = wl.WORKLOADS["prefill_hq12_hkv12_d64_t512_f32"]
+    case = wl.workload_prefill_case(w)
+    announce("prefill workload 512 tokens 12/12 d64 f32")
+    got, gk, gv = run_prefill(case)
+    ref, kp, vp, count = oracle_prefill(case)
+    assert count == 131328
+    assert_bitwise(gk, kp, "K pool after write")
+    assert_within(got, ref, 1e-5, 0.0, "prefill 512")
+
+
+PREFILL_CASES = [
+    # hq, hkv, d, ps, dtype, starts, lens, gap
+    (12, 3, 64, 16, "f32", [0, 63, 255, 512], [17, 64, 129, 257], 0),   # heterogeneous
+    (12, 3, 64, 16, "f32", [64] * 4, [64] * 4, 0),                      # history-64-at-64
+    (12, 12, 64, 16, "f32", [0] * 16, [16] * 16, 0),                    # 16x16
+    (8, 2, 128, 32, "bf16", [0, 33, 100], [1, 47, 300], 5),
+    (40, 8, 128, 16, "f16", [3000], [70], 0),
+    (4, 4, 64, 1, "f32", [5, 0], [20, 33], 2),
+    (16, 1, 128, 16, "bf16", [0], [129], 0),
+]
+
+
+@pytest.mark.parametrize("c", PREFILL_CASES,
+                         ids=lambda c: "hq{}_hkv{}_d{}_ps{}_{}_{}segs".format(*c[:5], len(c[5])))
+def test_prefill_cases(c):
+    hq, hkv, d, ps, dtype, starts, lens, gap = c
+    announce(f"prefill {c}")
+    rng = wl.rng_for([500, hq, hkv, d, ps, len(starts)])
+    case = wl.make_prefill_case(rng, hq=hq, hkv=hkv, head_dim=d, page_size=ps, dtype=dtype,
+                                lens=lens, starts=starts, gap_rows=gap)
+    got, _, _ = run_prefill(case, out_fill=7.0)
+    ref, _, _, _ = oracle_prefill(case)
+    covered = case.token_table_index >= 0
+    assert np.all(got[~covered] == 7.0), "rows outside every segment must stay untouched"
+    assert_within(got[covered], ref[covered], *tolerance(dtype), f"prefill {c}")
