@@ -120,14 +120,7 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
     a.num_splits = num_splits;
     a.qscale = scale * pa::kLog2e;
 
-    // Waves per workgroup: enough that one window pass covers the split's rows when the
-    // context is at the table's capacity (a host-side bound; lengths live on the device).
-    const int rows_per_wave_window = (64 / (head_dim * elem_bytes(kv_dtype) / 16)) * 4;
-    const int64_t cap = (int64_t)max_pages_per_seq * page_size;
-    const int64_t chunk = (cap + num_splits - 1) / num_splits;
-    int waves = (int)((chunk + rows_per_wave_window - 1) / rows_per_wave_window);
-    waves = waves < 1 ? 1 : (waves > 8 ? 8 : waves);
-    return launched(pa::launch_decode(a, kv_dtype, head_dim, waves, (hipStream_t)stream));
+    return launched(pa::launch_decode(a, kv_dtype, head_dim, (hipStream_t)stream));
 }
 
 int paged_attn_combine(const float* partial_o, const float* partial_ml, int num_seqs,

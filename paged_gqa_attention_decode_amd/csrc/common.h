@@ -71,17 +71,29 @@ constexpr int kDppQuadXor1 = 0xb1;     // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4e;     // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <- lane 7-i within 8
 constexpr int kDppMirror = 0x140;      // row_mirror: lane i <- lane 15-i within 16
+constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i <- lane (i+8) mod 16 (= xor 8)
+
+// Exchanges across 16-lane rows go through the LDS crossbar: ds_swizzle for xor 16 (inside
+// each half-wave) and ds_bpermute for xor 32.  (The gfx950 permlane16/32 row swaps would
+// stay in the VALU, but this compiler folds their two results as if they were equal, so
+// they are not used.)
+__device__ __forceinline__ float lane_xor16(float v) {
+    // swizzle bitmask mode: and 0x1f, or 0, xor 0x10
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),
+                                                                 0x401f));
+}
+__device__ __forceinline__ float lane_xor32(float v) { return __shfl_xor(v, 32); }
 
 // All-reduce over aligned groups of N lanes (N a power of two, 1..64).  Every lane of a
-// group ends with the bit-identical result: each step adds the same two operands.
+// group ends with the bit-identical result: each step combines the same two operands.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
     if constexpr (N >= 2) v += dpp_mov<kDppQuadXor1>(v);
     if constexpr (N >= 4) v += dpp_mov<kDppQuadXor2>(v);
     if constexpr (N >= 8) v += dpp_mov<kDppHalfMirror>(v);
     if constexpr (N >= 16) v += dpp_mov<kDppMirror>(v);
-    if constexpr (N >= 32) v += __shfl_xor(v, 16);
-    if constexpr (N >= 64) v += __shfl_xor(v, 32);
+    if constexpr (N >= 32) v += lane_xor16(v);
+    if constexpr (N >= 64) v += lane_xor32(v);
     return v;
 }
 
@@ -91,8 +103,26 @@ __device__ __forceinline__ float group_max(float v) {
     if constexpr (N >= 4) v = fmaxf(v, dpp_mov<kDppQuadXor2>(v));
     if constexpr (N >= 8) v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
     if constexpr (N >= 16) v = fmaxf(v, dpp_mov<kDppMirror>(v));
-    if constexpr (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
-    if constexpr (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+    if constexpr (N >= 32) v = fmaxf(v, lane_xor16(v));
+    if constexpr (N >= 64) v = fmaxf(v, lane_xor32(v));
+    return v;
+}
+
+// Reduction ACROSS the groups of N lanes of a wave (lanes with the same index within their
+// group combine): the complement of group_sum / group_max.
+template <int N>
+__device__ __forceinline__ float across_groups_sum(float v) {
+    if constexpr (N <= 8) v += dpp_mov<kDppRor8>(v);
+    if constexpr (N <= 16) v += lane_xor16(v);
+    if constexpr (N <= 32) v += lane_xor32(v);
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ float across_groups_max(float v) {
+    if constexpr (N <= 8) v = fmaxf(v, dpp_mov<kDppRor8>(v));
+    if constexpr (N <= 16) v = fmaxf(v, lane_xor16(v));
+    if constexpr (N <= 32) v = fmaxf(v, lane_xor32(v));
     return v;
 }
 
@@ -148,8 +178,7 @@ struct KvWriteArgs {
 };
 
 // Launchers (one translation unit each).  Return the hipError_t of the launch.
-hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int waves,
-                         hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int q_blocks,
                           hipStream_t stream);

@@ -21,8 +21,11 @@
 //         after the reduction, the D3-6 pitfall about divergent shuffles).
 //   table the sequence's page-table row (or a slice of it) is staged in LDS once; page ids are
 //         clamped into [0, num_pages) as they are staged.
-//   merge lane groups merge by shuffles, waves through LDS; the workgroup writes the split's
-//         (m, l) in natural-log units and the unnormalised O.
+//   merge lane groups merge with a DPP row rotation and LDS-crossbar lane exchanges (no LDS
+//         storage), waves through LDS; the workgroup writes the split's (m, l) in
+//         natural-log units and the unnormalised O.
+#include <algorithm>
+
 #include "common.h"
 
 namespace pa {
@@ -32,23 +35,48 @@ constexpr int kMaxWaves = 8;
 constexpr int kTableCap = 1024;  // page-table entries staged in LDS at a time
 constexpr int kWindowRows = 4;   // U: rows per lane group per window
 
+constexpr int kStreamLds = 64 * 1024;  // LDS for stream states at the largest head group
+
+template <typename KV, int D>
+struct DecodeGeom {
+    static constexpr int EPL = 16 / KV::kBytes;  // elements per lane load
+    static constexpr int LPR = D / EPL;          // lanes per row
+    static constexpr int RPI = 64 / LPR;         // rows per wave-wide load = streams per wave
+    // Most waves per workgroup: every stream keeps up to 8 heads x D floats in LDS.
+    static constexpr int kWaves = (kStreamLds / (8 * D * 4) / RPI) < kMaxWaves
+                                      ? (kStreamLds / (8 * D * 4) / RPI)
+                                      : kMaxWaves;
+};
+
+// Dynamic LDS of one workgroup: staged page ids, then per stream (wave x lane group) and
+// head the running max m, the sum l, the merge factor f, and the D-wide accumulator.
+__host__ __device__ constexpr size_t decode_lds_bytes(int streams, int gh, int d) {
+    return (size_t)kTableCap * 4 + (size_t)streams * gh * 4 * 4 + (size_t)streams * gh * d * 4;
+}
+
 template <typename KV, int D, int GH>
-__global__ void __launch_bounds__(kMaxWaves * 64) decode_split_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
+    decode_split_kernel(DecodeArgs a) {
     using T = typename KV::storage;
-    constexpr int EPL = 16 / KV::kBytes;  // elements per lane load
-    constexpr int LPR = D / EPL;          // lanes per row
-    constexpr int RPI = 64 / LPR;         // rows per wave-wide load
+    using G = DecodeGeom<KV, D>;
+    constexpr int EPL = G::EPL;
+    constexpr int LPR = G::LPR;
+    constexpr int RPI = G::RPI;
     constexpr int U = kWindowRows;
     constexpr int WROWS = RPI * U;        // rows per wave per window
-    static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "row must map onto a wave");
+    constexpr int TPT = kTableCap / 64;   // table entries staged per thread (>= 64 threads)
+    static_assert(LPR >= 8 && LPR <= 64 && (64 % LPR) == 0, "row must map onto a wave");
 
-    __shared__ int s_tbl[kTableCap];
-    __shared__ float s_m[kMaxWaves][GH];
-    __shared__ float s_l[kMaxWaves][GH];
-    __shared__ float s_o[kMaxWaves][GH][D];
-
+    extern __shared__ __align__(16) float lds[];
     const int nthreads = blockDim.x;
     const int nwaves = nthreads >> 6;
+    const int streams = nwaves * RPI;
+    int* s_tbl = reinterpret_cast<int*>(lds);
+    float* s_m = lds + kTableCap;          // [streams][GH]
+    float* s_l = s_m + streams * GH;       // [streams][GH]
+    float* s_f = s_l + streams * GH;       // [streams][GH]
+    float* s_o = s_f + 2 * streams * GH;   // [streams][GH][D] (16-byte aligned)
+
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -62,23 +90,8 @@ __global__ void __launch_bounds__(kMaxWaves * 64) decode_split_kernel(DecodeArgs
     const int h0 = kvh * a.group + hg * a.heads_per_wg;
     const int nh = min(GH, a.group - hg * a.heads_per_wg);
 
-    // Stage the whole page-table row when it fits: independent of the context length, so
-    // this load overlaps the length load instead of following it.
-    const int32_t* trow = a.page_table + (size_t)b * a.max_pages;
-    const bool whole_row = a.max_pages <= kTableCap;
-    if (whole_row) {
-        for (int i = tid; i < a.max_pages; i += nthreads)
-            s_tbl[i] = clampi(trow[i], 0, a.num_pages - 1);
-    }
-
-    const int cap = a.max_pages << a.page_shift;
-    const int ctx = clampi(a.context_lens[b], 0, cap);
-    const int S = a.num_splits;
-    const int chunk = (ctx + S - 1) / S;
-    const int lo = min(split * chunk, ctx);
-    const int hi = min(lo + chunk, ctx);
-
-    // Query slices, pre-multiplied by scale*log2(e) so that scores are in base-2 units.
+    // Everything that does not depend on the context length is requested first, so the
+    // query, the page-table row and the length arrive in one memory round trip.
     float qv[GH][EPL];
 #pragma unroll
     for (int j = 0; j < GH; ++j) {
@@ -87,12 +100,40 @@ __global__ void __launch_bounds__(kMaxWaves * 64) decode_split_kernel(DecodeArgs
 #pragma unroll
         for (int e = 0; e < EPL; e += 4) {
             const float4 t = *reinterpret_cast<const float4*>(qp + e);
-            qv[j][e + 0] = t.x * a.qscale;
-            qv[j][e + 1] = t.y * a.qscale;
-            qv[j][e + 2] = t.z * a.qscale;
-            qv[j][e + 3] = t.w * a.qscale;
+            qv[j][e + 0] = t.x;
+            qv[j][e + 1] = t.y;
+            qv[j][e + 2] = t.z;
+            qv[j][e + 3] = t.w;
         }
     }
+    const int32_t* trow = a.page_table + (size_t)b * a.max_pages;
+    const bool whole_row = a.max_pages <= kTableCap;
+    int tv[TPT];
+    if (whole_row) {
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + k * nthreads;
+            tv[k] = (i < a.max_pages) ? trow[i] : 0;
+        }
+    }
+    const int cap = a.max_pages << a.page_shift;
+    const int ctx = clampi(a.context_lens[b], 0, cap);
+    const int S = a.num_splits;
+    const int chunk = (ctx + S - 1) / S;
+    const int lo = min(split * chunk, ctx);
+    const int hi = min(lo + chunk, ctx);
+    if (whole_row) {
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + k * nthreads;
+            if (i < a.max_pages) s_tbl[i] = clampi(tv[k], 0, a.num_pages - 1);
+        }
+    }
+    // Scores are kept in base-2 units: q is pre-multiplied by scale*log2(e).
+#pragma unroll
+    for (int j = 0; j < GH; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[j][e] *= a.qscale;
 
     float m[GH], l[GH], o[GH][EPL];
 #pragma unroll
@@ -109,67 +150,92 @@ __global__ void __launch_bounds__(kMaxWaves * 64) decode_split_kernel(DecodeArgs
     const int pshift = a.page_shift;
     const int pmask = (1 << pshift) - 1;
 
-    // Rows [r0, r1) of this split; page ids come from s_tbl[(t >> pshift) - pg0].
-    auto process = [&](int r0, int r1, int pg0) {
-        for (int w0 = r0 + wave * WROWS; w0 < r1; w0 += nwaves * WROWS) {
-            uint4 kr[U], vr[U];
-            bool ok[U];
+    // One window: U rows per lane group starting at w0, rows past r1 clamped onto row
+    // r1 - 1 (a valid address, cache hits) and flagged, so no branch guards the loads.
+    struct Window {
+        uint4 k[U], v[U];
+        bool ok[U];
+    };
+    auto load_window = [&](Window& W, int w0, int r1, int pg0) {
+        int t[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int t = w0 + u * RPI + lg;
-                ok[u] = t < r1;
-                kr[u] = make_uint4(0, 0, 0, 0);
-                vr[u] = make_uint4(0, 0, 0, 0);
-                if (ok[u]) {
-                    const size_t page = (size_t)s_tbl[(t >> pshift) - pg0];
-                    const size_t row = ((page << pshift) | (size_t)(t & pmask)) * slot_stride;
-                    kr[u] = *reinterpret_cast<const uint4*>(kbase + row);
-                    vr[u] = *reinterpret_cast<const uint4*>(vbase + row);
-                }
-            }
-            float sc[U][GH];
+        for (int u = 0; u < U; ++u) {
+            const int tt = w0 + u * RPI + lg;
+            W.ok[u] = tt < r1;
+            t[u] = min(tt, r1 - 1);
+        }
+        int pg[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float kf[EPL];
-                widen16<KV>(kr[u], kf);
+        for (int u = 0; u < U; ++u) pg[u] = s_tbl[(t[u] >> pshift) - pg0];
 #pragma unroll
-                for (int j = 0; j < GH; ++j) {
-                    float d = 0.f;
+        for (int u = 0; u < U; ++u) {
+            const size_t row = (((size_t)pg[u] << pshift) | (size_t)(t[u] & pmask)) * slot_stride;
+            W.k[u] = *reinterpret_cast<const uint4*>(kbase + row);
+            W.v[u] = *reinterpret_cast<const uint4*>(vbase + row);
+        }
+    };
+    auto compute_window = [&](const Window& W) {
+        float sc[U][GH];
 #pragma unroll
-                    for (int e = 0; e < EPL; ++e) d = fmaf(qv[j][e], kf[e], d);
-                    d = group_sum<LPR>(d);
-                    sc[u][j] = ok[u] ? d : -INFINITY;
-                }
-            }
-            float p[U][GH];
+        for (int u = 0; u < U; ++u) {
+            float kf[EPL];
+            widen16<KV>(W.k[u], kf);
 #pragma unroll
             for (int j = 0; j < GH; ++j) {
-                float mx = m[j];
+                float d = 0.f;
 #pragma unroll
-                for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][j]);
-                const float ms = (mx == -INFINITY) ? 0.f : mx;
-                const float alpha = fast_exp2(m[j] - ms);
-                float ps = 0.f;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    p[u][j] = fast_exp2(sc[u][j] - ms);
-                    ps += p[u][j];
-                }
-                l[j] = fmaf(l[j], alpha, ps);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) o[j][e] *= alpha;
-                m[j] = mx;
+                for (int e = 0; e < EPL; ++e) d = fmaf(qv[j][e], kf[e], d);
+                d = group_sum<LPR>(d);
+                sc[u][j] = W.ok[u] ? d : -INFINITY;
             }
+        }
+        float p[U][GH];
+#pragma unroll
+        for (int j = 0; j < GH; ++j) {
+            float mx = m[j];
+#pragma unroll
+            for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][j]);
+            const float ms = (mx == -INFINITY) ? 0.f : mx;
+            const float alpha = fast_exp2(m[j] - ms);
+            float ps = 0.f;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float vf[EPL];
-                widen16<KV>(vr[u], vf);
-#pragma unroll
-                for (int j = 0; j < GH; ++j) {
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) o[j][e] = fmaf(p[u][j], vf[e], o[j][e]);
-                }
+                p[u][j] = fast_exp2(sc[u][j] - ms);
+                ps += p[u][j];
             }
+            l[j] = fmaf(l[j], alpha, ps);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[j][e] *= alpha;
+            m[j] = mx;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[EPL];
+            widen16<KV>(W.v[u], vf);
+#pragma unroll
+            for (int j = 0; j < GH; ++j) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[j][e] = fmaf(p[u][j], vf[e], o[j][e]);
+            }
+        }
+    };
+    // Rows [r0, r1) of this split (r0 < r1).  Two register windows alternate: the next
+    // window's loads are issued before the current window is computed.
+    auto process = [&](int r0, int r1, int pg0) {
+        const int step = nwaves * WROWS;
+        int w = r0 + wave * WROWS;
+        Window A, B;
+        if (w < r1) load_window(A, w, r1, pg0);
+        while (w < r1) {
+            int wn = w + step;
+            if (wn < r1) load_window(B, wn, r1, pg0);
+            compute_window(A);
+            w = wn;
+            if (w >= r1) break;
+            wn = w + step;
+            if (wn < r1) load_window(A, wn, r1, pg0);
+            compute_window(B);
+            w = wn;
         }
     };
 
@@ -189,102 +255,114 @@ __global__ void __launch_bounds__(kMaxWaves * 64) decode_split_kernel(DecodeArgs
         }
     }
 
-    // Merge the lane groups of this wave (same rows' heads, different rows).
+    // Every stream (wave, lane group) leaves its state in LDS; no cross-lane exchange.
+    const int stream = wave * RPI + lg;
 #pragma unroll
     for (int j = 0; j < GH; ++j) {
-        float mw = m[j];
+        float4* dst = reinterpret_cast<float4*>(s_o + ((size_t)stream * GH + j) * D + li * EPL);
 #pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off));
-        const float ms = (mw == -INFINITY) ? 0.f : mw;
-        const float f = fast_exp2(m[j] - ms);
-        float lw = l[j] * f;
-#pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            float x = o[j][e] * f;
-#pragma unroll
-            for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
-            o[j][e] = x;
-        }
-        m[j] = mw;
-        l[j] = lw;
+        for (int e = 0; e < EPL; e += 4)
+            dst[e / 4] = make_float4(o[j][e], o[j][e + 1], o[j][e + 2], o[j][e + 3]);
     }
-    if (lg == 0) {
-#pragma unroll
-        for (int j = 0; j < GH; ++j)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) s_o[wave][j][li * EPL + e] = o[j][e];
-    }
-    if (lane == 0) {
+    if (li == 0) {
 #pragma unroll
         for (int j = 0; j < GH; ++j) {
-            s_m[wave][j] = m[j];
-            s_l[wave][j] = l[j];
+            s_m[stream * GH + j] = m[j];
+            s_l[stream * GH + j] = l[j];
         }
     }
     __syncthreads();
 
-    // Merge the waves and write the split's partial.
+    // Merge, phase 1: per (stream, head) the factor f = exp(m_s - M), M the split's maximum.
+    for (int idx = tid; idx < streams * GH; idx += nthreads) {
+        const int j = idx % GH;
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < streams; ++s2) M = fmaxf(M, s_m[s2 * GH + j]);
+        const float ms = (M == -INFINITY) ? 0.f : M;
+        s_f[idx] = fast_exp2(s_m[idx] - ms);
+    }
+    __syncthreads();
+
+    // Merge, phase 2: one weighted sum per output element of the split's partial.
     for (int idx = tid; idx < GH * D; idx += nthreads) {
         const int j = idx / D;
         const int d = idx - j * D;
         if (j >= nh) continue;
-        float M = -INFINITY;
-        for (int w = 0; w < nwaves; ++w) M = fmaxf(M, s_m[w][j]);
-        const float ms = (M == -INFINITY) ? 0.f : M;
-        float L = 0.f, O = 0.f;
-        for (int w = 0; w < nwaves; ++w) {
-            const float f = fast_exp2(s_m[w][j] - ms);
-            L = fmaf(s_l[w][j], f, L);
-            O = fmaf(s_o[w][j][d], f, O);
+        float O0 = 0.f, O1 = 0.f;
+        int s2 = 0;
+        for (; s2 + 1 < streams; s2 += 2) {
+            O0 = fmaf(s_o[((size_t)s2 * GH + j) * D + d], s_f[s2 * GH + j], O0);
+            O1 = fmaf(s_o[((size_t)(s2 + 1) * GH + j) * D + d], s_f[(s2 + 1) * GH + j], O1);
         }
+        if (s2 < streams) O0 = fmaf(s_o[((size_t)s2 * GH + j) * D + d], s_f[s2 * GH + j], O0);
         const size_t slot = ((size_t)b * a.num_q_heads + h0 + j) * S + split;
-        a.partial_o[slot * D + d] = O;
+        a.partial_o[slot * D + d] = O0 + O1;
         if (d == 0) {
+            float L = 0.f, M = -INFINITY;
+            for (int s3 = 0; s3 < streams; ++s3) {
+                L = fmaf(s_l[s3 * GH + j], s_f[s3 * GH + j], L);
+                M = fmaxf(M, s_m[s3 * GH + j]);
+            }
             a.partial_ml[2 * slot] = (L > 0.f) ? M * kLn2 : -INFINITY;
             a.partial_ml[2 * slot + 1] = L;
         }
     }
 }
 
-template <typename KV, int D>
-hipError_t launch_typed(const DecodeArgs& a, int waves, hipStream_t stream) {
-    const dim3 grid(a.num_splits, a.num_kv_heads * a.head_groups, a.num_seqs);
-    const dim3 block(waves * 64);
-    switch (a.heads_per_wg) {
-#define PA_DECODE_CASE(GH)                                                         \
-    case GH:                                                                       \
-        hipLaunchKernelGGL((decode_split_kernel<KV, D, GH>), grid, block, 0, stream, a); \
-        break;
-        PA_DECODE_CASE(1)
-        PA_DECODE_CASE(2)
-        PA_DECODE_CASE(3)
-        PA_DECODE_CASE(4)
-        PA_DECODE_CASE(5)
-        PA_DECODE_CASE(6)
-        PA_DECODE_CASE(7)
-        PA_DECODE_CASE(8)
-#undef PA_DECODE_CASE
-        default:
-            return hipErrorInvalidValue;
+template <typename KV, int D, int GH>
+hipError_t launch_gh(const DecodeArgs& a, int waves, hipStream_t stream) {
+    using G = DecodeGeom<KV, D>;
+    const size_t lds = decode_lds_bytes(waves * G::RPI, GH, D);
+    // Workgroups asking for more than 64 KB of LDS opt in once per instantiation.
+    static size_t opted = 64 * 1024;
+    if (lds > opted) {
+        hipError_t e = hipFuncSetAttribute((const void*)decode_split_kernel<KV, D, GH>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        opted = lds;
     }
+    const dim3 grid(a.num_splits, a.num_kv_heads * a.head_groups, a.num_seqs);
+    hipLaunchKernelGGL((decode_split_kernel<KV, D, GH>), grid, dim3(waves * 64), lds, stream, a);
     return hipGetLastError();
+}
+
+template <typename KV, int D>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+    using G = DecodeGeom<KV, D>;
+    // Waves per workgroup: enough for one window pass to cover a split of the table's
+    // capacity (lengths live on the device), at most G::kWaves.  The choice depends only on
+    // the split size, head_dim and dtype, never on the batch or the head grouping, so a
+    // sequence's result is bit-identical whatever it is batched with, and a GQA group gives
+    // the same bits as the equivalent MHA call.
+    const int64_t cap = (int64_t)a.max_pages << a.page_shift;
+    const int64_t chunk = (cap + a.num_splits - 1) / a.num_splits;
+    const int64_t rows_per_pass = (int64_t)G::RPI * kWindowRows;
+    int waves = (int)std::min<int64_t>(G::kWaves, (chunk + rows_per_pass - 1) / rows_per_pass);
+    waves = std::max(waves, 1);
+    switch (a.heads_per_wg) {
+        case 1: return launch_gh<KV, D, 1>(a, waves, stream);
+        case 2: return launch_gh<KV, D, 2>(a, waves, stream);
+        case 3: return launch_gh<KV, D, 3>(a, waves, stream);
+        case 4: return launch_gh<KV, D, 4>(a, waves, stream);
+        case 5: return launch_gh<KV, D, 5>(a, waves, stream);
+        case 6: return launch_gh<KV, D, 6>(a, waves, stream);
+        case 7: return launch_gh<KV, D, 7>(a, waves, stream);
+        case 8: return launch_gh<KV, D, 8>(a, waves, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, int waves,
-                         hipStream_t stream) {
-    if (waves < 1 || waves > kMaxWaves) return hipErrorInvalidValue;
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
     if (head_dim == 64) {
-        if (kv_dtype == 0) return launch_typed<F32, 64>(a, waves, stream);
-        if (kv_dtype == 1) return launch_typed<F16, 64>(a, waves, stream);
-        return launch_typed<BF16, 64>(a, waves, stream);
+        if (kv_dtype == 0) return launch_typed<F32, 64>(a, stream);
+        if (kv_dtype == 1) return launch_typed<F16, 64>(a, stream);
+        return launch_typed<BF16, 64>(a, stream);
     }
-    if (kv_dtype == 0) return launch_typed<F32, 128>(a, waves, stream);
-    if (kv_dtype == 1) return launch_typed<F16, 128>(a, waves, stream);
-    return launch_typed<BF16, 128>(a, waves, stream);
+    if (kv_dtype == 0) return launch_typed<F32, 128>(a, stream);
+    if (kv_dtype == 1) return launch_typed<F16, 128>(a, stream);
+    return launch_typed<BF16, 128>(a, stream);
 }
 
 }  // namespace pa

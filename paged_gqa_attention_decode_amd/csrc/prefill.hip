@@ -184,8 +184,7 @@ __global__ void __launch_bounds__(kWaves * 64) prefill_kernel(PrefillArgs a) {
                 s[st][i] = (rvalid && key <= qend) ? sacc[st][i] : -INFINITY;
                 tmax = fmaxf(tmax, s[st][i]);
             }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = across_groups_max<16>(tmax);  // over the 4 lane groups holding this row
         const float mn = fmaxf(m, tmax);
         const float ms = (mn == -INFINITY) ? 0.f : mn;
         const float alpha = fast_exp2(m - ms);
@@ -212,8 +211,7 @@ __global__ void __launch_bounds__(kWaves * 64) prefill_kernel(PrefillArgs a) {
                 for (int dt = 0; dt < NC; ++dt) oacc[dt] = mfma16(vf[st][i][dt], p[st][i], oacc[dt]);
     }
 
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    lsum = across_groups_sum<16>(lsum);
     if (g == 0) {
         s_m[wave][c16] = m;
         s_l[wave][c16] = lsum;
