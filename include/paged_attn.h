@@ -109,6 +109,38 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
                       float* partial_ml, void* stream);
 
 /*
+ * Single-launch decode step: the page write of the current token, the split-KV partials and
+ * their merge in ONE kernel (crucible README, "Split-position attention": the second
+ * dispatch costs about what the split gains; minfer D3-6, section 3.3 and section 5: per-layer
+ * dispatch and exposed latency are the residual).  The result equals
+ *     kv_page_write(current token) ; paged_attn_decode ; paged_attn_combine
+ * on the same arguments, to within f32 rounding (the merge is the same arithmetic).
+ *
+ *   k_new, v_new    [num_seqs][num_kv_heads][head_dim] kv_dtype, device: the K/V of each
+ *                   sequence's current token, which sits at position context_lens[b] - 1;
+ *                   it is stored into its page (bit-exact) and read from k_new/v_new here
+ *   k_pages,v_pages written at that one slot per (sequence, KV head), read elsewhere
+ *   partial_o, partial_ml  split workspace as for paged_attn_decode (left holding the
+ *                   partials)
+ *   counters        [num_seqs][num_kv_heads * ceil((Hq/Hkv) / 8)] uint32, device: zero
+ *                   before the first call; every call leaves them zero again (the last split
+ *                   of a group resets its counter), so the buffer is reused without clearing
+ *   out             [num_seqs][num_q_heads][head_dim] f32, device, written
+ * All other arguments and rules as for paged_attn_decode.  Calls that share a counters
+ * buffer must not overlap in time (enqueue them on one stream).
+ */
+int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new,
+                            void* k_pages, void* v_pages, pa_dtype kv_dtype,
+                            const int32_t* page_table, const int32_t* context_lens,
+                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int page_size, int num_pages, int max_pages_per_seq, float scale,
+                            int num_splits, float* partial_o, float* partial_ml,
+                            uint32_t* counters, float* out, void* stream);
+
+/* Number of uint32 counters paged_attn_decode_fused needs, or 0 for invalid arguments. */
+size_t paged_attn_decode_fused_counters(int num_seqs, int num_q_heads, int num_kv_heads);
+
+/*
  * Merge of split partials ([crucible-readme] "Split-position attention": rescale each chunk
  * by exp(m_chunk - m_global) and merge; [minfer-d3-6] Excerpt F: idle splits weigh zero):
  *     M      = max over splits with l_s > 0 of m_s

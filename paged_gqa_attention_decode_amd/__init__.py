@@ -20,7 +20,8 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_ELAUNCH = 0, -1, -2, -3
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 
 C_FUNCTIONS = ("paged_attn_status_string", "paged_attn_decode_workspace_bytes",
-               "paged_attn_decode", "paged_attn_combine", "paged_attn_prefill",
+               "paged_attn_decode", "paged_attn_decode_fused",
+               "paged_attn_decode_fused_counters", "paged_attn_combine", "paged_attn_prefill",
                "kv_page_write")
 
 
@@ -48,12 +49,16 @@ def raw_library():
         lib.paged_attn_decode_workspace_bytes.argtypes = [i, i, i, i]
         lib.paged_attn_decode_workspace_bytes.restype = ctypes.c_size_t
         lib.paged_attn_decode.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, f, i, p, p, p]
+        lib.paged_attn_decode_fused.argtypes = [p, p, p, p, p, i, p, p, i, i, i, i, i, i, i, f,
+                                                i, p, p, p, p, p]
+        lib.paged_attn_decode_fused_counters.argtypes = [i, i, i]
+        lib.paged_attn_decode_fused_counters.restype = ctypes.c_size_t
         lib.paged_attn_combine.argtypes = [p, p, i, i, i, i, p, p]
         lib.paged_attn_prefill.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, i, i, i, f,
                                            p, p]
         lib.kv_page_write.argtypes = [p, p, p, p, i, p, p, p, i, i, i, i, i, i, i, p]
-        for name in ("paged_attn_decode", "paged_attn_combine", "paged_attn_prefill",
-                     "kv_page_write"):
+        for name in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_combine",
+                     "paged_attn_prefill", "kv_page_write"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -137,6 +142,47 @@ def paged_attn_decode(q, k_pages, v_pages, page_table, context_lens, scale: floa
         page_table.shape[1], float(scale), S, _dev(partial_o, "partial_o", torch.float32),
         _dev(partial_ml, "partial_ml", torch.float32), _stream_handle(stream))
     _ok("paged_attn_decode", rc)
+
+
+def paged_attn_decode_fused_counters(num_seqs: int, num_q_heads: int,
+                                     num_kv_heads: int) -> int:
+    return int(raw_library().paged_attn_decode_fused_counters(num_seqs, num_q_heads,
+                                                               num_kv_heads))
+
+
+def paged_attn_decode_fused(q, k_new, v_new, k_pages, v_pages, page_table, context_lens,
+                            scale: float, partial_o, partial_ml, counters, out,
+                            stream=None) -> None:
+    """One-launch decode step: writes the current token (k_new/v_new [B,Hkv,D]) into its
+    page, computes the split partials and merges them into out [B,Hq,D] f32.  counters is a
+    uint32 buffer (int32 tensor) of paged_attn_decode_fused_counters(...) entries, zero
+    before the first call; each call leaves it zero."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    P, ps, Hkv, Dk = k_pages.shape
+    S = partial_o.shape[2] if partial_o.dim() == 4 else -1
+    if Dk != D or tuple(v_pages.shape) != tuple(k_pages.shape) or v_pages.dtype != k_pages.dtype:
+        raise ValueError("k_pages / v_pages shapes or dtypes disagree with q")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (B, Hkv, D) or t.dtype != k_pages.dtype:
+            raise ValueError(f"{name} must be [B, Hkv, D] in the cache dtype")
+    if tuple(partial_o.shape) != (B, Hq, S, D) or tuple(partial_ml.shape) != (B, Hq, S, 2):
+        raise ValueError("partial_o must be [B,Hq,S,D] and partial_ml [B,Hq,S,2]")
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B,Hq,D]")
+    need = paged_attn_decode_fused_counters(B, Hq, Hkv)
+    if counters.dtype != torch.int32 or counters.numel() < need:
+        raise ValueError(f"counters must be an int32 tensor of at least {need} entries")
+    rc = raw_library().paged_attn_decode_fused(
+        _dev(q, "q", torch.float32, 3), _dev(k_new, "k_new", ndim=3),
+        _dev(v_new, "v_new", ndim=3), _dev(k_pages, "k_pages", ndim=4),
+        _dev(v_pages, "v_pages", ndim=4), _kv_dtype(k_pages),
+        _dev(page_table, "page_table", torch.int32, 2),
+        _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D, ps, P,
+        page_table.shape[1], float(scale), S, _dev(partial_o, "partial_o", torch.float32),
+        _dev(partial_ml, "partial_ml", torch.float32), _dev(counters, "counters"),
+        _dev(out, "out", torch.float32, 3), _stream_handle(stream))
+    _ok("paged_attn_decode_fused", rc)
 
 
 def paged_attn_combine(partial_o, partial_ml, out, stream=None) -> None:

@@ -74,14 +74,16 @@ size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int head
     return (size_t)bytes;
 }
 
-int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
-                      pa_dtype kv_dtype, const int32_t* page_table,
-                      const int32_t* context_lens, int num_seqs, int num_q_heads,
-                      int num_kv_heads, int head_dim, int page_size, int num_pages,
-                      int max_pages_per_seq, float scale, int num_splits, float* partial_o,
-                      float* partial_ml, void* stream) {
-    if (num_seqs < 0) return PA_EINVAL;
-    if (num_seqs == 0) return PA_OK;
+}  // extern "C"
+
+namespace {
+
+// Validation and argument packing shared by the two decode entry points.
+int make_decode_args(const float* q, const void* k_pages, const void* v_pages, int kv_dtype,
+                     const int32_t* page_table, const int32_t* context_lens, int num_seqs,
+                     int num_q_heads, int num_kv_heads, int head_dim, int page_size,
+                     int num_pages, int max_pages_per_seq, float scale, int num_splits,
+                     float* partial_o, float* partial_ml, pa::DecodeArgs* out) {
     if (!q || !k_pages || !v_pages || !page_table || !context_lens || !partial_o || !partial_ml)
         return PA_EINVAL;
     int rc = check_pages(kv_dtype, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
@@ -94,13 +96,12 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
     if ((int64_t)num_seqs * max_pages_per_seq > kI32Max ||
         (int64_t)num_seqs * num_q_heads * num_splits * head_dim > kI32Max * 4LL)
         return PA_EINVAL;
-
     const int group = num_q_heads / num_kv_heads;
     const int head_groups = (group + kMaxHeadsPerWg - 1) / kMaxHeadsPerWg;
     const int heads_per_wg = (group + head_groups - 1) / head_groups;
     if ((int64_t)num_kv_heads * head_groups > kMaxGridYZ) return PA_EUNSUPPORTED;
 
-    pa::DecodeArgs a;
+    pa::DecodeArgs a = {};
     a.q = q;
     a.k_pages = k_pages;
     a.v_pages = v_pages;
@@ -119,8 +120,60 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
     a.max_pages = max_pages_per_seq;
     a.num_splits = num_splits;
     a.qscale = scale * pa::kLog2e;
+    *out = a;
+    return PA_OK;
+}
 
-    return launched(pa::launch_decode(a, kv_dtype, head_dim, (hipStream_t)stream));
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
+                      pa_dtype kv_dtype, const int32_t* page_table,
+                      const int32_t* context_lens, int num_seqs, int num_q_heads,
+                      int num_kv_heads, int head_dim, int page_size, int num_pages,
+                      int max_pages_per_seq, float scale, int num_splits, float* partial_o,
+                      float* partial_ml, void* stream) {
+    if (num_seqs < 0) return PA_EINVAL;
+    if (num_seqs == 0) return PA_OK;
+    pa::DecodeArgs a;
+    int rc = make_decode_args(q, k_pages, v_pages, kv_dtype, page_table, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                              max_pages_per_seq, scale, num_splits, partial_o, partial_ml, &a);
+    if (rc != PA_OK) return rc;
+    return launched(pa::launch_decode(a, kv_dtype, head_dim, false, (hipStream_t)stream));
+}
+
+size_t paged_attn_decode_fused_counters(int num_seqs, int num_q_heads, int num_kv_heads) {
+    if (num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads)
+        return 0;
+    const int group = num_q_heads / num_kv_heads;
+    const int head_groups = (group + kMaxHeadsPerWg - 1) / kMaxHeadsPerWg;
+    return (size_t)num_seqs * num_kv_heads * head_groups;
+}
+
+int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new,
+                            void* k_pages, void* v_pages, pa_dtype kv_dtype,
+                            const int32_t* page_table, const int32_t* context_lens,
+                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int page_size, int num_pages, int max_pages_per_seq, float scale,
+                            int num_splits, float* partial_o, float* partial_ml,
+                            uint32_t* counters, float* out, void* stream) {
+    if (num_seqs < 0) return PA_EINVAL;
+    if (num_seqs == 0) return PA_OK;
+    if (!k_new || !v_new || !counters || !out) return PA_EINVAL;
+    pa::DecodeArgs a;
+    int rc = make_decode_args(q, k_pages, v_pages, kv_dtype, page_table, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                              max_pages_per_seq, scale, num_splits, partial_o, partial_ml, &a);
+    if (rc != PA_OK) return rc;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_pages_w = k_pages;
+    a.v_pages_w = v_pages;
+    a.counters = counters;
+    a.out = out;
+    return launched(pa::launch_decode(a, kv_dtype, head_dim, true, (hipStream_t)stream));
 }
 
 int paged_attn_combine(const float* partial_o, const float* partial_ml, int num_seqs,

@@ -130,6 +130,86 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
 
+// ---------------------------------------------------------------- split merge
+
+constexpr int kMergeChunk = 32;  // splits whose partials are in flight at once
+
+// Merge of one (sequence, head) row's split partials for one float4 column of the output:
+// ml[s] = (m_s, l_s) in natural-log units, po[s * stride4] = the column of O_s.  One pass
+// with a running maximum: every load of a chunk is issued before any of its values is used,
+// so a chunk costs one memory round trip.  Idle splits (l_s = 0) contribute nothing, whatever
+// their O holds.  Shared by the merge kernel and the fused decode, so both give the same bits.
+//
+// COHERENT: the partials were written by other workgroups of the running launch, so every
+// load is a device-scope (relaxed atomic) one, served by the device's coherence point and
+// never by a stale line of this XCD's L2; 8-byte accesses, two per float4.
+template <bool COHERENT>
+__device__ __forceinline__ float2 load_ml(const float2* p) {
+    if constexpr (COHERENT) {
+        const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p),
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+    } else {
+        return *p;
+    }
+}
+
+template <bool COHERENT>
+__device__ __forceinline__ float4 load_o4(const float4* p) {
+    if constexpr (COHERENT) {
+        const float2 lo = load_ml<true>(reinterpret_cast<const float2*>(p));
+        const float2 hi = load_ml<true>(reinterpret_cast<const float2*>(p) + 1);
+        return make_float4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+        return *p;
+    }
+}
+
+template <bool COHERENT = false>
+__device__ __forceinline__ float4 merge_splits(const float2* ml, const float4* po, int S,
+                                               int stride4) {
+    float M = -INFINITY;
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
+        float2 v[kMergeChunk];
+        float4 o[kMergeChunk];
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) {
+            const int s = min(s0 + k, S - 1);
+            v[k] = load_ml<COHERENT>(ml + s);
+            o[k] = load_o4<COHERENT>(po + (size_t)s * stride4);
+        }
+        float cm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) {
+            const bool live = (s0 + k < S) && v[k].y > 0.f;
+            cm = fmaxf(cm, live ? v[k].x : -INFINITY);
+        }
+        if (cm == -INFINITY) continue;  // nothing live in this chunk
+        const float Mn = fmaxf(M, cm);
+        const float r = fast_exp2((M - Mn) * kLog2e);  // 0 while M is still -inf
+        L *= r;
+        acc.x *= r;
+        acc.y *= r;
+        acc.z *= r;
+        acc.w *= r;
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) {
+            const bool live = (s0 + k < S) && v[k].y > 0.f;
+            const float w = live ? fast_exp2((v[k].x - Mn) * kLog2e) : 0.f;
+            L = live ? fmaf(w, v[k].y, L) : L;
+            acc.x = live ? fmaf(w, o[k].x, acc.x) : acc.x;
+            acc.y = live ? fmaf(w, o[k].y, acc.y) : acc.y;
+            acc.z = live ? fmaf(w, o[k].z, acc.z) : acc.z;
+            acc.w = live ? fmaf(w, o[k].w, acc.w) : acc.w;
+        }
+        M = Mn;
+    }
+    if (!(L > 0.f)) return make_float4(0.f, 0.f, 0.f, 0.f);
+    return make_float4(acc.x / L, acc.y / L, acc.z / L, acc.w / L);
+}
+
 // ---------------------------------------------------------------- launcher arguments
 
 struct DecodeArgs {
@@ -140,6 +220,13 @@ struct DecodeArgs {
     const int32_t* context_lens;
     float* partial_o;
     float* partial_ml;
+    // single-launch step only (null otherwise)
+    const void* k_new;       // [B][Hkv][D] current token's K and V
+    const void* v_new;
+    void* k_pages_w;         // the pools again, writable: the current token's slot
+    void* v_pages_w;
+    uint32_t* counters;      // [B][Hkv * head_groups] finished splits, reset by the last
+    float* out;              // [B][Hq][D]
     int num_seqs, num_q_heads, num_kv_heads, group, head_groups, heads_per_wg;
     int page_shift, num_pages, max_pages, num_splits;
     float qscale;  // scale * log2(e)
@@ -178,7 +265,8 @@ struct KvWriteArgs {
 };
 
 // Launchers (one translation unit each).  Return the hipError_t of the launch.
-hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, bool fused,
+                         hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int q_blocks,
                           hipStream_t stream);

@@ -54,9 +54,18 @@ __host__ __device__ constexpr size_t decode_lds_bytes(int streams, int gh, int d
     return (size_t)kTableCap * 4 + (size_t)streams * gh * 4 * 4 + (size_t)streams * gh * d * 4;
 }
 
-template <typename KV, int D, int GH>
-__global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
-    decode_split_kernel(DecodeArgs a) {
+// A split partial leaves the workgroup by a plain store, or, when another workgroup of the
+// same launch merges it, by a device-scope one (written through this XCD's L2).
+template <bool COHERENT>
+__device__ __forceinline__ void store_partial(float* p, float v) {
+    if constexpr (COHERENT)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+
+template <typename KV, int D, int GH, bool FUSED>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     using T = typename KV::storage;
     using G = DecodeGeom<KV, D>;
     constexpr int EPL = G::EPL;
@@ -68,6 +77,7 @@ __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
     static_assert(LPR >= 8 && LPR <= 64 && (64 % LPR) == 0, "row must map onto a wave");
 
     extern __shared__ __align__(16) float lds[];
+    __shared__ int s_last;  // single-launch step: this workgroup finished the group's last split
     const int nthreads = blockDim.x;
     const int nwaves = nthreads >> 6;
     const int streams = nwaves * RPI;
@@ -90,8 +100,21 @@ __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
     const int h0 = kvh * a.group + hg * a.heads_per_wg;
     const int nh = min(GH, a.group - hg * a.heads_per_wg);
 
-    // Everything that does not depend on the context length is requested first, so the
-    // query, the page-table row and the length arrive in one memory round trip.
+    // Nothing here depends on the context length, so the page-table row, the length and the
+    // query are requested together, the table first: the K/V loads wait only for the table,
+    // and the query's round trip overlaps them.
+    const int32_t* trow = a.page_table + (size_t)b * a.max_pages;
+    const bool whole_row = a.max_pages <= kTableCap;
+    int tv[TPT];
+    if (whole_row) {
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+            const int i = tid + k * nthreads;
+            tv[k] = (i < a.max_pages) ? trow[i] : 0;
+        }
+    }
+    const int cap = a.max_pages << a.page_shift;
+    const int ctx = clampi(a.context_lens[b], 0, cap);
     float qv[GH][EPL];
 #pragma unroll
     for (int j = 0; j < GH; ++j) {
@@ -106,18 +129,6 @@ __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
             qv[j][e + 3] = t.w;
         }
     }
-    const int32_t* trow = a.page_table + (size_t)b * a.max_pages;
-    const bool whole_row = a.max_pages <= kTableCap;
-    int tv[TPT];
-    if (whole_row) {
-#pragma unroll
-        for (int k = 0; k < TPT; ++k) {
-            const int i = tid + k * nthreads;
-            tv[k] = (i < a.max_pages) ? trow[i] : 0;
-        }
-    }
-    const int cap = a.max_pages << a.page_shift;
-    const int ctx = clampi(a.context_lens[b], 0, cap);
     const int S = a.num_splits;
     const int chunk = (ctx + S - 1) / S;
     const int lo = min(split * chunk, ctx);
@@ -129,11 +140,7 @@ __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
             if (i < a.max_pages) s_tbl[i] = clampi(tv[k], 0, a.num_pages - 1);
         }
     }
-    // Scores are kept in base-2 units: q is pre-multiplied by scale*log2(e).
-#pragma unroll
-    for (int j = 0; j < GH; ++j)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) qv[j][e] *= a.qscale;
+    const float qscale = a.qscale;  // scale * log2(e): scores in base-2 units
 
     float m[GH], l[GH], o[GH][EPL];
 #pragma unroll
@@ -149,6 +156,16 @@ __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
     const T* vbase = reinterpret_cast<const T*>(a.v_pages) + (size_t)kvh * D + li * EPL;
     const int pshift = a.page_shift;
     const int pmask = (1 << pshift) - 1;
+    // Single-launch step: the current token (position ctx - 1) is read from k_new / v_new;
+    // its pool slot is written by this launch and read by none of its workgroups.
+    const int t_new = FUSED ? ctx - 1 : -1;
+    const T* knew = nullptr;
+    const T* vnew = nullptr;
+    if constexpr (FUSED) {
+        const size_t off = ((size_t)b * a.num_kv_heads + kvh) * D + li * EPL;
+        knew = reinterpret_cast<const T*>(a.k_new) + off;
+        vnew = reinterpret_cast<const T*>(a.v_new) + off;
+    }
 
     // One window: U rows per lane group starting at w0, rows past r1 clamped onto row
     // r1 - 1 (a valid address, cache hits) and flagged, so no branch guards the loads.
@@ -170,8 +187,14 @@ __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const size_t row = (((size_t)pg[u] << pshift) | (size_t)(t[u] & pmask)) * slot_stride;
-            W.k[u] = *reinterpret_cast<const uint4*>(kbase + row);
-            W.v[u] = *reinterpret_cast<const uint4*>(vbase + row);
+            const T* kp = kbase + row;
+            const T* vp = vbase + row;
+            if constexpr (FUSED) {
+                kp = (t[u] == t_new) ? knew : kp;
+                vp = (t[u] == t_new) ? vnew : vp;
+            }
+            W.k[u] = *reinterpret_cast<const uint4*>(kp);
+            W.v[u] = *reinterpret_cast<const uint4*>(vp);
         }
     };
     auto compute_window = [&](const Window& W) {
@@ -186,7 +209,7 @@ __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) d = fmaf(qv[j][e], kf[e], d);
                 d = group_sum<LPR>(d);
-                sc[u][j] = W.ok[u] ? d : -INFINITY;
+                sc[u][j] = W.ok[u] ? d * qscale : -INFINITY;
             }
         }
         float p[U][GH];
@@ -239,6 +262,7 @@ __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
         }
     };
 
+    int pg0_last = 0;  // first table entry of the last staged slice
     if (whole_row) {
         __syncthreads();
         if (lo < hi) process(lo, hi, 0);
@@ -252,6 +276,22 @@ __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
                 s_tbl[i] = clampi(trow[pg0 + i], 0, a.num_pages - 1);
             __syncthreads();
             process(max(lo, pg0 << pshift), min(hi, (pg0 + n) << pshift), pg0);
+            pg0_last = pg0;
+        }
+    }
+
+    // Single-launch step: the split holding the current token stores it into its page
+    // (head group 0 only; one row per KV head).
+    if constexpr (FUSED) {
+        if (hg == 0 && wave == 0 && lg == 0 && t_new >= lo && t_new < hi) {
+            const size_t page = (size_t)s_tbl[(t_new >> pshift) - pg0_last];
+            const size_t row =
+                (((page << pshift) | (size_t)(t_new & pmask)) * slot_stride) + (size_t)kvh * D +
+                li * EPL;
+            *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.k_pages_w) + row) =
+                *reinterpret_cast<const uint4*>(knew);
+            *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.v_pages_w) + row) =
+                *reinterpret_cast<const uint4*>(vnew);
         }
     }
 
@@ -296,37 +336,92 @@ __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
         }
         if (s2 < streams) O0 = fmaf(s_o[((size_t)s2 * GH + j) * D + d], s_f[s2 * GH + j], O0);
         const size_t slot = ((size_t)b * a.num_q_heads + h0 + j) * S + split;
-        a.partial_o[slot * D + d] = O0 + O1;
+        store_partial<FUSED>(a.partial_o + slot * D + d, O0 + O1);
         if (d == 0) {
             float L = 0.f, M = -INFINITY;
             for (int s3 = 0; s3 < streams; ++s3) {
                 L = fmaf(s_l[s3 * GH + j], s_f[s3 * GH + j], L);
                 M = fmaxf(M, s_m[s3 * GH + j]);
             }
-            a.partial_ml[2 * slot] = (L > 0.f) ? M * kLn2 : -INFINITY;
-            a.partial_ml[2 * slot + 1] = L;
+            store_partial<FUSED>(a.partial_ml + 2 * slot, (L > 0.f) ? M * kLn2 : -INFINITY);
+            store_partial<FUSED>(a.partial_ml + 2 * slot + 1, L);
         }
+    }
+
+    if constexpr (FUSED) {
+        // The last of the group's S workgroups to finish merges their partials.  The partials
+        // travel by device-scope stores and loads (written through to, and read from, the
+        // device's coherence point), so no fence has to write back or invalidate a whole L2
+        // (each XCD has its own, and that costs microseconds per workgroup).  Every wave waits
+        // until its stores are acknowledged, the barrier gathers the waves, and only then is
+        // the workgroup counted; the last one counted reads after its count returned.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        uint32_t* counter = a.counters + ((size_t)b * a.num_kv_heads + kvh) * a.head_groups + hg;
+        if (tid == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == (uint32_t)(S - 1)) ? 1 : 0;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        constexpr int D4 = D / 4;
+        for (int idx = tid; idx < nh * D4; idx += nthreads) {
+            const int j = idx / D4;
+            const int c = idx - j * D4;
+            const size_t row = (size_t)b * a.num_q_heads + h0 + j;
+            const float2* ml = reinterpret_cast<const float2*>(a.partial_ml) + row * S;
+            const float4* po = reinterpret_cast<const float4*>(a.partial_o) + row * S * D4 + c;
+            reinterpret_cast<float4*>(a.out)[row * D4 + c] = merge_splits<true>(ml, po, S, D4);
+        }
+        if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
+// Split partials only (paged_attn_decode).
 template <typename KV, int D, int GH>
+__global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
+    decode_split_kernel(DecodeArgs a) {
+    decode_body<KV, D, GH, false>(a);
+}
+
+// The single-launch step (paged_attn_decode_fused): page write, partials, last-split merge.
+template <typename KV, int D, int GH>
+__global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
+    decode_step_kernel(DecodeArgs a) {
+    decode_body<KV, D, GH, true>(a);
+}
+
+template <typename KV, int D, int GH, bool FUSED>
+const void* decode_kernel_ptr() {
+    if constexpr (FUSED)
+        return (const void*)decode_step_kernel<KV, D, GH>;
+    else
+        return (const void*)decode_split_kernel<KV, D, GH>;
+}
+
+template <typename KV, int D, int GH, bool FUSED>
 hipError_t launch_gh(const DecodeArgs& a, int waves, hipStream_t stream) {
     using G = DecodeGeom<KV, D>;
     const size_t lds = decode_lds_bytes(waves * G::RPI, GH, D);
     // Workgroups asking for more than 64 KB of LDS opt in once per instantiation.
     static size_t opted = 64 * 1024;
     if (lds > opted) {
-        hipError_t e = hipFuncSetAttribute((const void*)decode_split_kernel<KV, D, GH>,
+        hipError_t e = hipFuncSetAttribute(decode_kernel_ptr<KV, D, GH, FUSED>(),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         opted = lds;
     }
     const dim3 grid(a.num_splits, a.num_kv_heads * a.head_groups, a.num_seqs);
-    hipLaunchKernelGGL((decode_split_kernel<KV, D, GH>), grid, dim3(waves * 64), lds, stream, a);
+    if constexpr (FUSED)
+        hipLaunchKernelGGL((decode_step_kernel<KV, D, GH>), grid, dim3(waves * 64), lds, stream, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<KV, D, GH>), grid, dim3(waves * 64), lds, stream,
+                           a);
     return hipGetLastError();
 }
 
-template <typename KV, int D>
+template <typename KV, int D, bool FUSED>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     using G = DecodeGeom<KV, D>;
     // Waves per workgroup: enough for one window pass to cover a split of the table's
@@ -340,29 +435,36 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     int waves = (int)std::min<int64_t>(G::kWaves, (chunk + rows_per_pass - 1) / rows_per_pass);
     waves = std::max(waves, 1);
     switch (a.heads_per_wg) {
-        case 1: return launch_gh<KV, D, 1>(a, waves, stream);
-        case 2: return launch_gh<KV, D, 2>(a, waves, stream);
-        case 3: return launch_gh<KV, D, 3>(a, waves, stream);
-        case 4: return launch_gh<KV, D, 4>(a, waves, stream);
-        case 5: return launch_gh<KV, D, 5>(a, waves, stream);
-        case 6: return launch_gh<KV, D, 6>(a, waves, stream);
-        case 7: return launch_gh<KV, D, 7>(a, waves, stream);
-        case 8: return launch_gh<KV, D, 8>(a, waves, stream);
+        case 1: return launch_gh<KV, D, 1, FUSED>(a, waves, stream);
+        case 2: return launch_gh<KV, D, 2, FUSED>(a, waves, stream);
+        case 3: return launch_gh<KV, D, 3, FUSED>(a, waves, stream);
+        case 4: return launch_gh<KV, D, 4, FUSED>(a, waves, stream);
+        case 5: return launch_gh<KV, D, 5, FUSED>(a, waves, stream);
+        case 6: return launch_gh<KV, D, 6, FUSED>(a, waves, stream);
+        case 7: return launch_gh<KV, D, 7, FUSED>(a, waves, stream);
+        case 8: return launch_gh<KV, D, 8, FUSED>(a, waves, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
+template <bool FUSED>
+hipError_t launch_all(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
+    if (head_dim == 64) {
+        if (kv_dtype == 0) return launch_typed<F32, 64, FUSED>(a, stream);
+        if (kv_dtype == 1) return launch_typed<F16, 64, FUSED>(a, stream);
+        return launch_typed<BF16, 64, FUSED>(a, stream);
+    }
+    if (kv_dtype == 0) return launch_typed<F32, 128, FUSED>(a, stream);
+    if (kv_dtype == 1) return launch_typed<F16, 128, FUSED>(a, stream);
+    return launch_typed<BF16, 128, FUSED>(a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
-    if (head_dim == 64) {
-        if (kv_dtype == 0) return launch_typed<F32, 64>(a, stream);
-        if (kv_dtype == 1) return launch_typed<F16, 64>(a, stream);
-        return launch_typed<BF16, 64>(a, stream);
-    }
-    if (kv_dtype == 0) return launch_typed<F32, 128>(a, stream);
-    if (kv_dtype == 1) return launch_typed<F16, 128>(a, stream);
-    return launch_typed<BF16, 128>(a, stream);
+hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, bool fused,
+                         hipStream_t stream) {
+    return fused ? launch_all<true>(a, kv_dtype, head_dim, stream)
+                 : launch_all<false>(a, kv_dtype, head_dim, stream);
 }
 
 }  // namespace pa

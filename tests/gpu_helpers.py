@@ -71,3 +71,15 @@ class DecodeRun:
         self.decode()
         torch.cuda.synchronize()
         return host(self.out)
+
+    def fused_step(self):
+        """The same step as one launch (paged_attn_decode_fused)."""
+        if not hasattr(self, "counters"):
+            B, Hq, D = self.case.q.shape
+            n = pa.paged_attn_decode_fused_counters(B, Hq, self.case.k_pages.shape[2])
+            self.counters = torch.zeros(n, dtype=torch.int32, device=DEV)
+        pa.paged_attn_decode_fused(self.q, self.k_new, self.v_new, self.kp, self.vp, self.table,
+                                   self.ctx, self.case.scale, self.po, self.pml, self.counters,
+                                   self.out)
+        torch.cuda.synchronize()
+        return host(self.out)

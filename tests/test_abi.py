@@ -28,7 +28,8 @@ def test_header_lists_the_four_entry_points():
     names = header_functions()
     for n in ("paged_attn_decode", "paged_attn_combine", "paged_attn_prefill",
               "kv_page_write", "paged_attn_decode_workspace_bytes",
-              "paged_attn_status_string"):
+              "paged_attn_status_string", "paged_attn_decode_fused",
+              "paged_attn_decode_fused_counters"):
         assert n in names
     assert set(names) == set(pa.C_FUNCTIONS)
 
@@ -100,6 +101,32 @@ def decode(**kw):
 ])
 def test_decode_validation(kw, status):
     assert decode(**kw) == status
+
+
+def test_fused_counters_and_validation():
+    lib = pa.raw_library()
+    assert pa.paged_attn_decode_fused_counters(1, 40, 8) == 8
+    assert pa.paged_attn_decode_fused_counters(16, 64, 8) == 128
+    assert pa.paged_attn_decode_fused_counters(2, 12 * 16, 12) == 2 * 12 * 2   # G=16: 2 groups
+    assert pa.paged_attn_decode_fused_counters(1, 41, 8) == 0
+    f = lib.paged_attn_decode_fused
+    # (q, k_new, v_new, kp, vp, dtype, table, ctx, B, Hq, Hkv, D, ps, P, maxp, scale, S,
+    #  po, pml, counters, out, stream)
+    good = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, 40, 8, 128, 16, 204, 204, 0.0884,
+            32, FAKE, FAKE, FAKE, FAKE, NULL]
+
+    def call(over):
+        args = list(good)
+        for k, v in over.items():
+            args[k] = v
+        return f(*args)
+
+    assert call({8: 0, 0: NULL}) == pa.PA_OK
+    for i in (0, 1, 2, 3, 4, 6, 7, 17, 18, 19, 20):
+        assert call({i: NULL}) == pa.PA_EINVAL, i
+    assert call({11: 96}) == pa.PA_EUNSUPPORTED
+    assert call({16: 0}) == pa.PA_EINVAL
+    assert call({9: 41}) == pa.PA_EINVAL
 
 
 def test_combine_validation():

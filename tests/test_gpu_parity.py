@@ -170,6 +170,53 @@ def test_decode_outlier_data():
     assert_within(out, ref, *tolerance("f16"), "decode outliers")
 
 
+# ----------------------------------------------------------------------------- fused step
+
+def _fused_checks(case, S=None, what=""):
+    """One-launch step vs the oracle, vs the three-kernel path (bit-identical), counters
+    left at zero, and a second call (reusing the counters) bit-identical to the first."""
+    fused = DecodeRun(case, num_splits=S)
+    out = fused.fused_step()
+    kp, vp, ref = oracle_step(case)
+    assert_bitwise(host(fused.kp), kp, f"{what} K pool after the fused write")
+    assert_bitwise(host(fused.vp), vp, f"{what} V pool after the fused write")
+    assert_within(out, ref, *tolerance(case.dtype), f"fused {what}")
+    assert int(fused.counters.abs().sum().item()) == 0, "counters must be left at zero"
+    again = fused.fused_step()
+    assert_bitwise(again, out, f"{what} second fused call")
+    three = DecodeRun(case, num_splits=S).step()
+    assert_bitwise(out, three, f"{what} fused vs write+decode+combine")
+    check_partials(fused, case, kp, vp)
+
+
+@pytest.mark.parametrize("name", DECODE_WORKLOADS)
+def test_decode_fused_workload(name):
+    w = wl.WORKLOADS[name]
+    case = wl.workload_decode_case(w)
+    announce(f"fused decode workload {name}")
+    _fused_checks(case, what=name)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 64, 4096])
+def test_decode_fused_split_counts(splits):
+    case = wl.workload_decode_case(wl.WORKLOADS["decode_hq28_hkv4_d128_ctx1641_f16"])
+    announce(f"fused decode 7B shape S={splits}")
+    _fused_checks(case, S=splits, what=f"S={splits}")
+
+
+@pytest.mark.parametrize("geom", [(40, 8, 128, 16, "f16", 32), (8, 2, 64, 16, "f32", 16),
+                                  (24, 2, 128, 32, "bf16", 8), (4, 4, 64, 1, "bf16", 5)],
+                         ids=lambda g: "hq{}_hkv{}_d{}_ps{}_{}_S{}".format(*g))
+def test_decode_fused_boundary_lengths(geom):
+    hq, hkv, d, ps, dtype, S = geom
+    announce(f"fused decode boundary lengths {geom}")
+    rng = wl.rng_for([310, hq, hkv, d, ps])
+    ctx = BOUNDARY_CTX if ps > 1 else [c for c in BOUNDARY_CTX if c <= 1100]
+    case = wl.make_decode_case(rng, batch=len(ctx), hq=hq, hkv=hkv, head_dim=d,
+                               page_size=ps, dtype=dtype, ctx=ctx, num_splits=S)
+    _fused_checks(case, what=f"boundary {geom}")
+
+
 # ----------------------------------------------------------------------------- combine alone
 
 @pytest.mark.parametrize("d,S", [(64, 1), (64, 16), (128, 32), (128, 33), (128, 4096)])
