@@ -23,7 +23,8 @@ __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     const int S = a.num_splits;
     const float2* ml = reinterpret_cast<const float2*>(a.partial_ml) + (size_t)row * S;
     const float4* po = reinterpret_cast<const float4*>(a.partial_o) + (size_t)row * S * TPR + c;
-    reinterpret_cast<float4*>(a.out)[(size_t)row * TPR + c] = merge_splits(ml, po, S, TPR);
+    const PlainPartials src{ml, po, TPR};
+    reinterpret_cast<float4*>(a.out)[(size_t)row * TPR + c] = merge_splits(src, S);
 }
 
 }  // namespace

@@ -134,40 +134,55 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x,
 
 constexpr int kMergeChunk = 32;  // splits whose partials are in flight at once
 
-// Merge of one (sequence, head) row's split partials for one float4 column of the output:
-// ml[s] = (m_s, l_s) in natural-log units, po[s * stride4] = the column of O_s.  One pass
-// with a running maximum: every load of a chunk is issued before any of its values is used,
-// so a chunk costs one memory round trip.  Idle splits (l_s = 0) contribute nothing, whatever
-// their O holds.  Shared by the merge kernel and the fused decode, so both give the same bits.
+// Where one row's split partials are read from, for one float4 column of the output:
+// ml(s) = (m_s, l_s) in natural-log units and o(s) = that column of O_s, for s < S.
 //
-// COHERENT: the partials were written by other workgroups of the running launch, so every
-// load is a device-scope (relaxed atomic) one, served by the device's coherence point and
-// never by a stale line of this XCD's L2; 8-byte accesses, two per float4.
-template <bool COHERENT>
-__device__ __forceinline__ float2 load_ml(const float2* p) {
-    if constexpr (COHERENT) {
-        const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p),
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
-    } else {
-        return *p;
+// Plain loads: the partials were written by an earlier launch.  A slot past S reads split
+// S - 1 again (a cache hit), so no branch guards the loads.
+struct PlainPartials {
+    const float2* ml;
+    const float4* po;
+    int stride4;  // float4s between the column's entries of consecutive splits
+    __device__ __forceinline__ float2 ml_at(int s, int S) const { return ml[min(s, S - 1)]; }
+    __device__ __forceinline__ float4 o_at(int s, int S) const {
+        return po[(size_t)min(s, S - 1) * stride4];
     }
-}
+};
 
-template <bool COHERENT>
-__device__ __forceinline__ float4 load_o4(const float4* p) {
-    if constexpr (COHERENT) {
-        const float2 lo = load_ml<true>(reinterpret_cast<const float2*>(p));
-        const float2 hi = load_ml<true>(reinterpret_cast<const float2*>(p) + 1);
-        return make_float4(lo.x, lo.y, hi.x, hi.y);
-    } else {
-        return *p;
+// Device-scope loads: the partials were written by other workgroups of the running launch
+// with device-scope stores, so each load has to be served by the device's coherence point,
+// never by a stale line in this XCD's L2 (the cache-policy bit below; 16 bytes per access
+// through a buffer resource whose base is uniform over the workgroup).  These loads are not
+// cache hits, so a slot past S issues none.
+constexpr int kDeviceScopeLoad = 16;  // buffer-instruction cache policy: device scope
+constexpr uint32_t kRawBufferWord3 = 0x00020000;  // untyped 32-bit buffer, no swizzle
+struct CoherentPartials {
+    __amdgpu_buffer_rsrc_t o_rsrc, ml_rsrc;
+    uint32_t o_off;     // bytes from o_rsrc's base to this column of split 0
+    uint32_t o_stride;  // bytes between consecutive splits
+    uint32_t ml_off;    // bytes from ml_rsrc's base to (m, l) of split 0
+    __device__ __forceinline__ float2 ml_at(int s, int S) const {
+        if (s >= S) return make_float2(-INFINITY, 0.f);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, ml_off + (uint32_t)s * 8u,
+                                                            0, kDeviceScopeLoad);
+        return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
     }
-}
+    __device__ __forceinline__ float4 o_at(int s, int S) const {
+        if (s >= S) return make_float4(0.f, 0.f, 0.f, 0.f);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(o_rsrc, o_off + (uint32_t)s * o_stride,
+                                                             0, kDeviceScopeLoad);
+        return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                           __uint_as_float(v[3]));
+    }
+};
 
-template <bool COHERENT = false>
-__device__ __forceinline__ float4 merge_splits(const float2* ml, const float4* po, int S,
-                                               int stride4) {
+// Merge of one (sequence, head) row's split partials for one float4 column of the output.
+// One pass with a running maximum: every load of a chunk is issued before any of its values
+// is used, so a chunk costs one memory round trip.  Idle splits (l_s = 0) contribute nothing,
+// whatever their O holds.  The merge kernel and the fused decode both call it, with the same
+// arithmetic whatever the source, so both give the same bits.
+template <typename Src>
+__device__ __forceinline__ float4 merge_splits(const Src& src, int S) {
     float M = -INFINITY;
     float L = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -176,9 +191,8 @@ __device__ __forceinline__ float4 merge_splits(const float2* ml, const float4* p
         float4 o[kMergeChunk];
 #pragma unroll
         for (int k = 0; k < kMergeChunk; ++k) {
-            const int s = min(s0 + k, S - 1);
-            v[k] = load_ml<COHERENT>(ml + s);
-            o[k] = load_o4<COHERENT>(po + (size_t)s * stride4);
+            v[k] = src.ml_at(s0 + k, S);
+            o[k] = src.o_at(s0 + k, S);
         }
         float cm = -INFINITY;
 #pragma unroll

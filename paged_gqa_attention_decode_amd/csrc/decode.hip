@@ -73,6 +73,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     constexpr int RPI = G::RPI;
     constexpr int U = kWindowRows;
     constexpr int WROWS = RPI * U;        // rows per wave per window
+    // Registers of q and of the accumulators (2 GH EPL) plus two windows of K/V (16 U).
+    constexpr bool kPrefetch = 2 * GH * EPL + 16 * U < 192;
     constexpr int TPT = kTableCap / 64;   // table entries staged per thread (>= 64 threads)
     static_assert(LPR >= 8 && LPR <= 64 && (64 % LPR) == 0, "row must map onto a wave");
 
@@ -243,10 +245,21 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         }
     };
     // Rows [r0, r1) of this split (r0 < r1).  Two register windows alternate: the next
-    // window's loads are issued before the current window is computed.
+    // window's loads are issued before the current window is computed.  Where q and the
+    // accumulators already take most registers (8 heads of 16-bit K/V), one window is
+    // loaded at a time and the second wave per SIMD that this frees room for hides the
+    // latency instead; the windows, and so the arithmetic, are the same either way.
     auto process = [&](int r0, int r1, int pg0) {
         const int step = nwaves * WROWS;
         int w = r0 + wave * WROWS;
+        if constexpr (!kPrefetch) {
+            for (; w < r1; w += step) {
+                Window A;
+                load_window(A, w, r1, pg0);
+                compute_window(A);
+            }
+            return;
+        }
         Window A, B;
         if (w < r1) load_window(A, w, r1, pg0);
         while (w < r1) {
@@ -366,13 +379,21 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         __syncthreads();
         if (!s_last) return;
         constexpr int D4 = D / 4;
+        // Buffer resources over this workgroup's rows of partials (bases uniform over the
+        // workgroup; at most 8 heads x 4096 splits x D floats, far below 2^31 bytes).
+        const size_t row0 = (size_t)b * a.num_q_heads + h0;
+        CoherentPartials src;
+        src.o_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.partial_o + row0 * S * D, 0,
+                                                       nh * S * D * 4, kRawBufferWord3);
+        src.ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.partial_ml + row0 * S * 2, 0,
+                                                        nh * S * 8, kRawBufferWord3);
+        src.o_stride = D * 4;
         for (int idx = tid; idx < nh * D4; idx += nthreads) {
             const int j = idx / D4;
             const int c = idx - j * D4;
-            const size_t row = (size_t)b * a.num_q_heads + h0 + j;
-            const float2* ml = reinterpret_cast<const float2*>(a.partial_ml) + row * S;
-            const float4* po = reinterpret_cast<const float4*>(a.partial_o) + row * S * D4 + c;
-            reinterpret_cast<float4*>(a.out)[row * D4 + c] = merge_splits<true>(ml, po, S, D4);
+            src.o_off = (uint32_t)((j * S * D + c * 4) * 4);
+            src.ml_off = (uint32_t)(j * S * 8);
+            reinterpret_cast<float4*>(a.out)[(row0 + j) * D4 + c] = merge_splits(src, S);
         }
         if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -381,14 +402,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 // Split partials only (paged_attn_decode).
 template <typename KV, int D, int GH>
 __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
-    decode_split_kernel(DecodeArgs a) {
+    __attribute__((amdgpu_waves_per_eu(2))) decode_split_kernel(DecodeArgs a) {
     decode_body<KV, D, GH, false>(a);
 }
 
 // The single-launch step (paged_attn_decode_fused): page write, partials, last-split merge.
 template <typename KV, int D, int GH>
 __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
-    decode_step_kernel(DecodeArgs a) {
+    __attribute__((amdgpu_waves_per_eu(2))) decode_step_kernel(DecodeArgs a) {
     decode_body<KV, D, GH, true>(a);
 }
 

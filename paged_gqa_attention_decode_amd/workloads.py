@@ -137,7 +137,7 @@ WORKLOADS = {
     "decode_b16_hq64_hkv8_d128_ctx64to4096_bf16": Workload(
         name="decode_b16_hq64_hkv8_d128_ctx64to4096_bf16", kind="decode", index=4, hq=64,
         hkv=8, head_dim=128, page_size=32, dtype="bf16", batch=16, ctx_range=(64, 4096),
-        num_pages=8192, num_splits=16, rotations=6,
+        num_pages=8192, num_splits=8, rotations=6,
         description="continuous-batching decode, 16 sequences in a shared 8192-page pool"),
 }
 
