@@ -162,7 +162,10 @@ int paged_attn_combine(const float* partial_o, const float* partial_ml, int num_
  * absolute position P = absolute_start + r of the sequence whose pages are listed in
  * page_table[table_index].  It attends to that sequence's positions 0 .. P inclusive:
  *     out[packed_start + r][h][:] = softmax_t(scale * q.K[t]) . V[t],  t in [0, P]
- * The caller writes the K/V of every attended position (including the chunk itself) first.
+ * The caller writes the K/V of every attended position (including the chunk itself) first,
+ * with finite values at every position 0 .. absolute_start + chunk_len - 1: rows are
+ * computed 16 at a time, and a masked position's weight is exactly 0, which does not cancel
+ * an infinity or NaN held at a later position of the same chunk.
  * Segments must not overlap in the packed dimension; rows not covered by any segment are
  * left untouched.
  *

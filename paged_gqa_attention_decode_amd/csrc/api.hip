@@ -230,6 +230,8 @@ int paged_attn_prefill(const float* q, const void* k_pages, const void* v_pages,
     a.max_pages = max_pages_per_seq;
     a.qscale = scale * pa::kLog2e;
     const int q_blocks = (max_chunk_len + 15) / 16;
+    if ((int64_t)q_blocks * num_q_heads > kI32Max) return PA_EUNSUPPORTED;
+    a.q_blocks = q_blocks;
     return launched(
         pa::launch_prefill(a, kv_dtype, head_dim, q_blocks, (hipStream_t)stream));
 }

@@ -263,6 +263,7 @@ struct PrefillArgs {
     float* out;
     int num_segs, num_tables, total_tokens, num_q_heads, num_kv_heads, group;
     int page_shift, num_pages, max_pages;
+    int q_blocks;  // 16-row query blocks of the longest segment
     float qscale;  // scale * log2(e)
 };
 
