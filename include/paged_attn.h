@@ -1,11 +1,12 @@
 /*
  * paged_attn.h — C ABI of the MI355X (gfx950) paged grouped-query attention library.
  *
- * Four operations over a block-paged KV cache:
- *   kv_page_write       scatter new K/V rows into their pages
- *   paged_attn_decode   one query row per sequence, split-KV partial softmax
- *   paged_attn_combine  log-sum-exp merge of the split partials
- *   paged_attn_prefill  causal attention for packed prompt segments
+ * Operations over a block-paged KV cache:
+ *   kv_page_write            scatter new K/V rows into their pages
+ *   paged_attn_decode        one query row per sequence, split-KV partial softmax
+ *   paged_attn_combine       log-sum-exp merge of the split partials
+ *   paged_attn_decode_fused  the three above for one decode step, in a single launch
+ *   paged_attn_prefill       causal attention for packed prompt segments
  *
  * Sources (the method these calls implement):
  *   [crucible-results] crucible, "Paged attention results" (docs/paged-attention-results.md):
@@ -23,7 +24,8 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library allocates
- *     nothing, keeps no state between calls and is re-entrant.
+ *     nothing, keeps no state between calls and is re-entrant (paged_attn_decode_fused keeps
+ *     its per-call state in the caller's counter buffer; see there).
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null stream).
  *     No call synchronises; ordering is stream order, so a kv_page_write enqueued before an
  *     attention call on the same stream is visible to it.

@@ -142,7 +142,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
             if (i < a.max_pages) s_tbl[i] = clampi(tv[k], 0, a.num_pages - 1);
         }
     }
-    const float qscale = a.qscale;  // scale * log2(e): scores in base-2 units
+    // Scores in base-2 units: q is scaled once by scale * log2(e) (here, after the table
+    // staging, so the preamble does not wait for q's round trip).
+#pragma unroll
+    for (int j = 0; j < GH; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[j][e] *= a.qscale;
 
     float m[GH], l[GH], o[GH][EPL];
 #pragma unroll
@@ -211,27 +216,36 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) d = fmaf(qv[j][e], kf[e], d);
                 d = group_sum<LPR>(d);
-                sc[u][j] = W.ok[u] ? d * qscale : -INFINITY;
+                sc[u][j] = W.ok[u] ? d : -INFINITY;
             }
         }
         float p[U][GH];
+        float alpha[GH];
+        bool moved = false;  // some running maximum of this lane changed
 #pragma unroll
         for (int j = 0; j < GH; ++j) {
             float mx = m[j];
 #pragma unroll
             for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][j]);
             const float ms = (mx == -INFINITY) ? 0.f : mx;
-            const float alpha = fast_exp2(m[j] - ms);
+            alpha[j] = fast_exp2(m[j] - ms);
+            moved |= mx != m[j];
             float ps = 0.f;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 p[u][j] = fast_exp2(sc[u][j] - ms);
                 ps += p[u][j];
             }
-            l[j] = fmaf(l[j], alpha, ps);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) o[j][e] *= alpha;
+            l[j] = fmaf(l[j], alpha[j], ps);
             m[j] = mx;
+        }
+        // Where no running maximum of the wave moved, every alpha is exp2(0) = 1 (or the
+        // accumulator is still all zeros), so the rescale is skipped without changing a bit.
+        if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+#pragma unroll
+            for (int j = 0; j < GH; ++j)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) o[j][e] *= alpha[j];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
