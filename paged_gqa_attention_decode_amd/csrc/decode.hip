@@ -9,49 +9,222 @@
 // gfx950 mapping
 //   grid  (num_splits, num_kv_heads * head_groups, num_seqs); one workgroup of `waves`
 //         64-lane waves serves up to GH query heads of one KV head over one split.
-//   rows  a K or V row is D * elt bytes (256 B for D=128 f16/bf16 and D=64 f32).  LPR lanes
-//         cover one row with one 16-byte load each, so one wave-wide load fetches RPI = 64/LPR
-//         rows.  Each lane group (LPR lanes) keeps its own online-softmax stream per head.
-//   window each wave takes U rows per lane group (RPI*U rows) and issues every K and V load of
+//   rows  one K or V row (D elements) is spread over one 16-lane DPP row of a wave: each
+//         lane holds D/16 elements (8, 16 or 32 bytes, one or two vector loads), and one
+//         wave-wide load fetches 4 rows.  Each 16-lane row keeps its own online-softmax
+//         stream.
+//   window each wave takes U rows per 16-lane row (4U rows) and issues every K and V load of
 //         the window before the first dependent instruction (the whole-window staging of the
-//         minfer 75 "D4-3" page, 3.2 Excerpt A/C); the window max gives one rescale per window
-//         (minfer D3-6, 3.2 Excerpt B).
-//   dots  each lane multiplies its slice for all GH heads; DPP row operations reduce the
-//         partial dots inside the lane group; every lane reduces (the validity select comes
-//         after the reduction, the D3-6 pitfall about divergent shuffles).
+//         minfer 75 "D4-3" page, 3.2 Excerpt A/C).
+//   dots  each lane multiplies its slice for all GH heads, then a reduce-scatter over the 16
+//         lanes leaves every lane with the full score of one head.  The heads sit in the
+//         lane's registers in a lane-dependent order (see slot_key), so each exchange step
+//         is a single DPP add: 8 heads cost 8 adds per row instead of 32 for an all-reduce.
+//         Every lane takes part in every step (the validity select comes after the
+//         reduction, the D3-6 pitfall about divergent shuffles).
+//   softmax each lane runs the online softmax of its own head only; the probabilities reach
+//         the PV products by DPP row broadcasts.  The accumulator is rescaled only when a
+//         head's maximum rises more than kLazyRescale above the reference it was scaled to;
+//         the true maximum is tracked beside it and the split's partial is normalised to it.
 //   table the sequence's page-table row (or a slice of it) is staged in LDS once; page ids are
 //         clamped into [0, num_pages) as they are staged.
-//   merge lane groups merge with a DPP row rotation and LDS-crossbar lane exchanges (no LDS
-//         storage), waves through LDS; the workgroup writes the split's (m, l) in
+//   merge every stream leaves (m, l, O) in LDS; the workgroup writes the split's (m, l) in
 //         natural-log units and the unnormalised O.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
 namespace pa {
 namespace {
 
+// f(std::integral_constant<int, I>) for I in [I0, I1): a loop whose index is a constant.
+template <int I0, int I1, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I0 < I1) {
+        f(std::integral_constant<int, I0>{});
+        static_for<I0 + 1, I1>(f);
+    }
+}
+
 constexpr int kMaxWaves = 8;
 constexpr int kTableCap = 1024;  // page-table entries staged in LDS at a time
-constexpr int kWindowRows = 4;   // U: rows per lane group per window
+constexpr int kWindowRows = 4;   // U: rows per 16-lane row per window
+constexpr int kLanesPerRow = 16;
+constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+
+// Base-2 headroom of the lazy rescale: probabilities are exp2(s - m_ref) <= 2^8.
+constexpr float kLazyRescale = 8.f;
 
 constexpr int kStreamLds = 64 * 1024;  // LDS for stream states at the largest head group
 
 template <typename KV, int D>
 struct DecodeGeom {
-    static constexpr int EPL = 16 / KV::kBytes;  // elements per lane load
-    static constexpr int LPR = D / EPL;          // lanes per row
-    static constexpr int RPI = 64 / LPR;         // rows per wave-wide load = streams per wave
+    static constexpr int EPL = D / kLanesPerRow;          // elements per lane and row
+    static constexpr int WPL = EPL * KV::kBytes / 4;      // 32-bit words per lane and row
     // Most waves per workgroup: every stream keeps up to 8 heads x D floats in LDS.
-    static constexpr int kWaves = (kStreamLds / (8 * D * 4) / RPI) < kMaxWaves
-                                      ? (kStreamLds / (8 * D * 4) / RPI)
+    static constexpr int kWaves = (kStreamLds / (8 * D * 4) / kRowsPerLoad) < kMaxWaves
+                                      ? (kStreamLds / (8 * D * 4) / kRowsPerLoad)
                                       : kMaxWaves;
 };
 
-// Dynamic LDS of one workgroup: staged page ids, then per stream (wave x lane group) and
-// head the running max m, the sum l, the merge factor f, and the D-wide accumulator.
+// Dynamic LDS of one workgroup: staged page ids, then per head and stream (wave x 16-lane
+// row) the reference maximum, the true maximum and the sum l, then per stream the GH x D
+// accumulators (padded by 16 bytes).
 __host__ __device__ constexpr size_t decode_lds_bytes(int streams, int gh, int d) {
-    return (size_t)kTableCap * 4 + (size_t)streams * gh * 4 * 4 + (size_t)streams * gh * d * 4;
+    return (size_t)kTableCap * 4 + (size_t)streams * gh * 3 * 4 + (size_t)streams * (gh * d + 4) * 4;
+}
+
+// ------------------------------------------------------------------ K/V row fragments
+
+// One lane's slice of one K or V row: WPL 32-bit words, moved as one or two 16-byte loads
+// (or one 8-byte load for 64 16-bit elements).
+template <int WPL>
+struct Frag {
+    uint32_t w[WPL];
+};
+
+template <int WPL>
+__device__ __forceinline__ void load_frag(Frag<WPL>& f, const void* p) {
+    if constexpr (WPL == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        f.w[0] = v.x;
+        f.w[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < WPL; i += 4) {
+            const uint4 v = reinterpret_cast<const uint4*>(p)[i / 4];
+            f.w[i] = v.x;
+            f.w[i + 1] = v.y;
+            f.w[i + 2] = v.z;
+            f.w[i + 3] = v.w;
+        }
+    }
+}
+
+template <int WPL>
+__device__ __forceinline__ void store_frag(void* p, const Frag<WPL>& f) {
+    if constexpr (WPL == 2) {
+        *reinterpret_cast<uint2*>(p) = make_uint2(f.w[0], f.w[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < WPL; i += 4)
+            reinterpret_cast<uint4*>(p)[i / 4] = make_uint4(f.w[i], f.w[i + 1], f.w[i + 2],
+                                                            f.w[i + 3]);
+    }
+}
+
+template <typename KV, int WPL>
+__device__ __forceinline__ void widen_frag(const Frag<WPL>& f, float* out) {
+    constexpr int per = 4 / KV::kBytes;
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) widen_word(KV{}, f.w[i], out + i * per);
+}
+
+// ------------------------------------------------------------------ head slots
+
+// The GH heads of a workgroup are split into power-of-two groups of 8, 4, 2 and 1 (the
+// binary digits of GH, largest first).  In group n (size N, first head B) lane li computes,
+// in its register B + r, the partial dot of head B + (r ^ slot_key<N>(li)).  The exchange
+// partners of the reduction are lane ^ 8 (row_ror:8), lane ^ 7 (row_half_mirror), lane ^ 2
+// and lane ^ 1 (quad_perm), in that order; slot_key is the linear map of the lane bits
+// under which the first log2(N) partners each flip exactly one key bit (from the high one
+// down) and the later ones none.  So at every step a lane adds its register to the
+// partner's register that holds the same head, and after the four steps the lane holds the
+// full sum of head B + slot_key<N>(li).  The summation tree is the same for every N (and
+// equal to the all-reduce used for N = 1), so a head's score has the same bits whatever
+// companions it has.
+template <int N>
+__device__ __forceinline__ int slot_key(int li) {
+    if constexpr (N == 8)
+        return (((li >> 3) & 1) << 2) | (((li >> 2) & 1) << 1) | (((li >> 1) ^ (li >> 2)) & 1);
+    if constexpr (N == 4) return (((li >> 3) & 1) << 1) | ((li >> 2) & 1);
+    if constexpr (N == 2) return (li >> 3) & 1;
+    return 0;
+}
+
+// The lowest lane of a 16-lane row whose key is H (inverse of slot_key with bit 0 clear).
+template <int N>
+__host__ __device__ constexpr int owner_lane(int H) {
+    return N == 8   ? 8 * ((H >> 2) & 1) + 4 * ((H >> 1) & 1) + 2 * ((H ^ (H >> 1)) & 1)
+           : N == 4 ? 8 * ((H >> 1) & 1) + 4 * (H & 1)
+           : N == 2 ? 8 * (H & 1)
+                    : 0;
+}
+
+// Lanes that store a group's softmax state (one per head; the others hold copies).
+template <int N>
+__device__ __forceinline__ bool is_owner(int li) {
+    if constexpr (N == 8) return (li & 1) == 0;
+    if constexpr (N == 4) return (li & 3) == 0;
+    if constexpr (N == 2) return (li & 7) == 0;
+    return li == 0;
+}
+
+template <int GH>
+struct HeadGroups {
+    static constexpr int count = ((GH >> 3) & 1) + ((GH >> 2) & 1) + ((GH >> 1) & 1) + (GH & 1);
+    static constexpr int size(int g) {
+        int k = 0;
+        for (int n = 8; n >= 1; n >>= 1)
+            if (GH & n) {
+                if (k == g) return n;
+                ++k;
+            }
+        return 0;
+    }
+    static constexpr int base(int g) {
+        int b = 0;
+        for (int k = 0; k < g; ++k) b += size(k);
+        return b;
+    }
+};
+
+constexpr int kDppRowRor8 = 0x128;      // lane i <- lane (i + 8) mod 16 (= i ^ 8)
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7 - i within 8 (= i ^ 7)
+constexpr int kDppQuadX2 = 0x4e;         // quad_perm [2,3,0,1] (= i ^ 2)
+constexpr int kDppQuadX1 = 0xb1;         // quad_perm [1,0,3,2] (= i ^ 1)
+template <int L>
+__device__ __forceinline__ float row_bcast(float v) {  // row_newbcast: lane L of each row
+    return dpp_mov<0x150 + L>(v);
+}
+
+// Reduce-scatter of one group's N partial dots (registers d[0..N)) over the 16 lanes.
+template <int N>
+__device__ __forceinline__ float reduce_scatter(const float* d) {
+    float r;
+    if constexpr (N == 8) {
+        const float a0 = d[0] + dpp_mov<kDppRowRor8>(d[4]);
+        const float a1 = d[1] + dpp_mov<kDppRowRor8>(d[5]);
+        const float a2 = d[2] + dpp_mov<kDppRowRor8>(d[6]);
+        const float a3 = d[3] + dpp_mov<kDppRowRor8>(d[7]);
+        const float b0 = a0 + dpp_mov<kDppRowHalfMirror>(a2);
+        const float b1 = a1 + dpp_mov<kDppRowHalfMirror>(a3);
+        r = b0 + dpp_mov<kDppQuadX2>(b1);
+    } else if constexpr (N == 4) {
+        const float a0 = d[0] + dpp_mov<kDppRowRor8>(d[2]);
+        const float a1 = d[1] + dpp_mov<kDppRowRor8>(d[3]);
+        r = a0 + dpp_mov<kDppRowHalfMirror>(a1);
+        r = r + dpp_mov<kDppQuadX2>(r);
+    } else if constexpr (N == 2) {
+        r = d[0] + dpp_mov<kDppRowRor8>(d[1]);
+        r = r + dpp_mov<kDppRowHalfMirror>(r);
+        r = r + dpp_mov<kDppQuadX2>(r);
+    } else {
+        r = d[0] + dpp_mov<kDppRowRor8>(d[0]);
+        r = r + dpp_mov<kDppRowHalfMirror>(r);
+        r = r + dpp_mov<kDppQuadX2>(r);
+    }
+    return r + dpp_mov<kDppQuadX1>(r);
+}
+
+// Value of head B + H of group (N, B) from the lane that owns it, in every lane of the row.
+template <int N, int H>
+__device__ __forceinline__ float from_owner(float v) {
+    if constexpr (N == 1)
+        return v;
+    else
+        return row_bcast<owner_lane<N>(H)>(v);
 }
 
 // A split partial leaves the workgroup by a plain store, or, when another workgroup of the
@@ -68,15 +241,16 @@ template <typename KV, int D, int GH, bool FUSED>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     using T = typename KV::storage;
     using G = DecodeGeom<KV, D>;
+    using HG = HeadGroups<GH>;
+    constexpr int NG = HG::count;
     constexpr int EPL = G::EPL;
-    constexpr int LPR = G::LPR;
-    constexpr int RPI = G::RPI;
+    constexpr int WPL = G::WPL;
+    constexpr int RPI = kRowsPerLoad;
     constexpr int U = kWindowRows;
     constexpr int WROWS = RPI * U;        // rows per wave per window
-    // Registers of q and of the accumulators (2 GH EPL) plus two windows of K/V (16 U).
-    constexpr bool kPrefetch = 2 * GH * EPL + 16 * U < 192;
+    // Registers of q and of the accumulators plus two windows of K/V.
+    constexpr bool kPrefetch = 2 * GH * EPL + 4 * U * WPL <= 208;
     constexpr int TPT = kTableCap / 64;   // table entries staged per thread (>= 64 threads)
-    static_assert(LPR >= 8 && LPR <= 64 && (64 % LPR) == 0, "row must map onto a wave");
 
     extern __shared__ __align__(16) float lds[];
     __shared__ int s_last;  // single-launch step: this workgroup finished the group's last split
@@ -84,16 +258,17 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const int nwaves = nthreads >> 6;
     const int streams = nwaves * RPI;
     int* s_tbl = reinterpret_cast<int*>(lds);
-    float* s_m = lds + kTableCap;          // [streams][GH]
-    float* s_l = s_m + streams * GH;       // [streams][GH]
-    float* s_f = s_l + streams * GH;       // [streams][GH]
-    float* s_o = s_f + 2 * streams * GH;   // [streams][GH][D] (16-byte aligned)
+    float* s_m = lds + kTableCap;          // [GH][streams] reference maximum
+    float* s_t = s_m + GH * streams;       // [GH][streams] true maximum
+    float* s_l = s_t + GH * streams;       // [GH][streams] sum
+    float* s_o = s_l + GH * streams;       // [streams][SOS]: per stream GH x D, then padding
+    constexpr int SOS = GH * D + 4;        // padded so the 4 rows of a wave hit other banks
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int lg = lane / LPR;  // row slot within a wave-wide load
-    const int li = lane % LPR;  // 16-byte column within the row
+    const int lg = lane / kLanesPerRow;  // row slot within a wave-wide load
+    const int li = lane % kLanesPerRow;  // slice of the row
 
     const int split = blockIdx.x;
     const int kvh = blockIdx.y / a.head_groups;
@@ -117,20 +292,28 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     }
     const int cap = a.max_pages << a.page_shift;
     const int ctx = clampi(a.context_lens[b], 0, cap);
+    // q in the lane's register order: register B + r of group (N, B) holds head
+    // B + (r ^ slot_key<N>(li)); padded heads repeat the last real one.
     float qv[GH][EPL];
+    static_for<0, NG>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        constexpr int N = HG::size(g);
+        constexpr int B = HG::base(g);
+        const int key = slot_key<N>(li);
 #pragma unroll
-    for (int j = 0; j < GH; ++j) {
-        const int h = h0 + min(j, nh - 1);  // padded heads repeat the last real one
-        const float* qp = a.q + ((size_t)b * a.num_q_heads + h) * D + li * EPL;
+        for (int r = 0; r < N; ++r) {
+            const int h = h0 + min(B + (r ^ key), nh - 1);
+            const float* qp = a.q + ((size_t)b * a.num_q_heads + h) * D + li * EPL;
 #pragma unroll
-        for (int e = 0; e < EPL; e += 4) {
-            const float4 t = *reinterpret_cast<const float4*>(qp + e);
-            qv[j][e + 0] = t.x;
-            qv[j][e + 1] = t.y;
-            qv[j][e + 2] = t.z;
-            qv[j][e + 3] = t.w;
+            for (int e = 0; e < EPL; e += 4) {
+                const float4 t = *reinterpret_cast<const float4*>(qp + e);
+                qv[B + r][e + 0] = t.x;
+                qv[B + r][e + 1] = t.y;
+                qv[B + r][e + 2] = t.z;
+                qv[B + r][e + 3] = t.w;
+            }
         }
-    }
+    });
     const int S = a.num_splits;
     const int chunk = (ctx + S - 1) / S;
     const int lo = min(split * chunk, ctx);
@@ -149,18 +332,26 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) qv[j][e] *= a.qscale;
 
-    float m[GH], l[GH], o[GH][EPL];
+    // Per group, for the lane's own head: the reference maximum the accumulator is scaled
+    // to, the true running maximum and the running sum.  Accumulators in head order.
+    float mr[NG], mt[NG], l[NG], o[GH][EPL];
 #pragma unroll
-    for (int j = 0; j < GH; ++j) {
-        m[j] = -INFINITY;
-        l[j] = 0.f;
+    for (int g = 0; g < NG; ++g) {
+        mr[g] = -INFINITY;
+        mt[g] = -INFINITY;
+        l[g] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < GH; ++j)
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
-    }
 
-    const size_t slot_stride = (size_t)a.num_kv_heads * D;  // elements between slots
-    const T* kbase = reinterpret_cast<const T*>(a.k_pages) + (size_t)kvh * D + li * EPL;
-    const T* vbase = reinterpret_cast<const T*>(a.v_pages) + (size_t)kvh * D + li * EPL;
+    // Row addresses: one 32x32->64-bit multiply of the pool row by the bytes between slots
+    // (Hkv * D * elt < 2^32), added to the lane's base.
+    const uint32_t slot_bytes = (uint32_t)a.num_kv_heads * (uint32_t)(D * KV::kBytes);
+    const size_t lane_off = ((size_t)kvh * D + li * EPL) * KV::kBytes;
+    const char* kbase = reinterpret_cast<const char*>(a.k_pages) + lane_off;
+    const char* vbase = reinterpret_cast<const char*>(a.v_pages) + lane_off;
     const int pshift = a.page_shift;
     const int pmask = (1 << pshift) - 1;
     // Single-launch step: the current token (position ctx - 1) is read from k_new / v_new;
@@ -174,10 +365,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         vnew = reinterpret_cast<const T*>(a.v_new) + off;
     }
 
-    // One window: U rows per lane group starting at w0, rows past r1 clamped onto row
+    // One window: U rows per 16-lane row starting at w0, rows past r1 clamped onto row
     // r1 - 1 (a valid address, cache hits) and flagged, so no branch guards the loads.
     struct Window {
-        uint4 k[U], v[U];
+        Frag<WPL> k[U], v[U];
         bool ok[U];
     };
     auto load_window = [&](Window& W, int w0, int r1, int pg0) {
@@ -193,69 +384,101 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         for (int u = 0; u < U; ++u) pg[u] = s_tbl[(t[u] >> pshift) - pg0];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const size_t row = (((size_t)pg[u] << pshift) | (size_t)(t[u] & pmask)) * slot_stride;
-            const T* kp = kbase + row;
-            const T* vp = vbase + row;
+            const uint32_t row = ((uint32_t)pg[u] << pshift) | (uint32_t)(t[u] & pmask);
+            const uint64_t off = (uint64_t)row * slot_bytes;
+            const void* kp = kbase + off;
+            const void* vp = vbase + off;
             if constexpr (FUSED) {
-                kp = (t[u] == t_new) ? knew : kp;
-                vp = (t[u] == t_new) ? vnew : vp;
+                kp = (t[u] == t_new) ? (const void*)knew : kp;
+                vp = (t[u] == t_new) ? (const void*)vnew : vp;
             }
-            W.k[u] = *reinterpret_cast<const uint4*>(kp);
-            W.v[u] = *reinterpret_cast<const uint4*>(vp);
+            load_frag(W.k[u], kp);
+            load_frag(W.v[u], vp);
         }
     };
     auto compute_window = [&](const Window& W) {
-        float sc[U][GH];
+        // Scores: every lane ends with its own head's score of each of the U rows.
+        float s[NG][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float kf[EPL];
-            widen16<KV>(W.k[u], kf);
+            widen_frag<KV>(W.k[u], kf);
+            float d[GH];
 #pragma unroll
             for (int j = 0; j < GH; ++j) {
-                float d = 0.f;
+                float acc = qv[j][0] * kf[0];
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) d = fmaf(qv[j][e], kf[e], d);
-                d = group_sum<LPR>(d);
-                sc[u][j] = W.ok[u] ? d : -INFINITY;
+                for (int e = 1; e < EPL; ++e) acc = fmaf(qv[j][e], kf[e], acc);
+                d[j] = acc;
             }
+            static_for<0, NG>([&](auto gc) {
+                constexpr int g = decltype(gc)::value;
+                const float r = reduce_scatter<HG::size(g)>(d + HG::base(g));
+                s[g][u] = W.ok[u] ? r : -INFINITY;
+            });
         }
-        float p[U][GH];
-        float alpha[GH];
-        bool moved = false;  // some running maximum of this lane changed
+        // Online softmax of the lane's heads, one rescale decision per window.
+        float mx[NG];
+        bool need = false;
 #pragma unroll
-        for (int j = 0; j < GH; ++j) {
-            float mx = m[j];
+        for (int g = 0; g < NG; ++g) {
+            float v = s[g][0];
 #pragma unroll
-            for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][j]);
-            const float ms = (mx == -INFINITY) ? 0.f : mx;
-            alpha[j] = fast_exp2(m[j] - ms);
-            moved |= mx != m[j];
-            float ps = 0.f;
+            for (int u = 1; u < U; ++u) v = fmaxf(v, s[g][u]);
+            mx[g] = v;
+            mt[g] = fmaxf(mt[g], v);
+            need |= v > mr[g] + kLazyRescale;
+        }
+        // Rescale only where some head of the wave outgrew its reference by more than the
+        // headroom; a head that did not keeps its reference and is multiplied by exactly 1,
+        // so its bits do not depend on its companions.
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+            float alpha[NG];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                p[u][j] = fast_exp2(sc[u][j] - ms);
-                ps += p[u][j];
+            for (int g = 0; g < NG; ++g) {
+                const bool up = mx[g] > mr[g] + kLazyRescale;
+                alpha[g] = up ? fast_exp2(mr[g] - mx[g]) : 1.f;  // a reference of -inf gives 0
+                mr[g] = up ? mx[g] : mr[g];
+                l[g] *= alpha[g];
             }
-            l[j] = fmaf(l[j], alpha[j], ps);
-            m[j] = mx;
+            static_for<0, NG>([&](auto gc) {
+                constexpr int g = decltype(gc)::value;
+                constexpr int N = HG::size(g);
+                constexpr int B = HG::base(g);
+                static_for<0, N>([&](auto hc) {
+                    constexpr int h = decltype(hc)::value;
+                    const float f = from_owner<N, h>(alpha[g]);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) o[B + h][e] *= f;
+                });
+            });
         }
-        // Where no running maximum of the wave moved, every alpha is exp2(0) = 1 (or the
-        // accumulator is still all zeros), so the rescale is skipped without changing a bit.
-        if (__builtin_amdgcn_ballot_w64(moved) != 0) {
+        float p[NG][U];
 #pragma unroll
-            for (int j = 0; j < GH; ++j)
+        for (int g = 0; g < NG; ++g) {
+            const float ms = (mr[g] == -INFINITY) ? 0.f : mr[g];
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) o[j][e] *= alpha[j];
+            for (int u = 0; u < U; ++u) p[g][u] = fast_exp2(s[g][u] - ms);
+            float ps = p[g][0];
+#pragma unroll
+            for (int u = 1; u < U; ++u) ps += p[g][u];
+            l[g] += ps;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float vf[EPL];
-            widen16<KV>(W.v[u], vf);
+            widen_frag<KV>(W.v[u], vf);
+            static_for<0, NG>([&](auto gc) {
+                constexpr int g = decltype(gc)::value;
+                constexpr int N = HG::size(g);
+                constexpr int B = HG::base(g);
+                static_for<0, N>([&](auto hc) {
+                    constexpr int h = decltype(hc)::value;
+                    const float pb = from_owner<N, h>(p[g][u]);
 #pragma unroll
-            for (int j = 0; j < GH; ++j) {
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) o[j][e] = fmaf(p[u][j], vf[e], o[j][e]);
-            }
+                    for (int e = 0; e < EPL; ++e) o[B + h][e] = fmaf(pb, vf[e], o[B + h][e]);
+                });
+            });
         }
     };
     // Rows [r0, r1) of this split (r0 < r1).  Two register windows alternate: the next
@@ -311,65 +534,85 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     // (head group 0 only; one row per KV head).
     if constexpr (FUSED) {
         if (hg == 0 && wave == 0 && lg == 0 && t_new >= lo && t_new < hi) {
-            const size_t page = (size_t)s_tbl[(t_new >> pshift) - pg0_last];
-            const size_t row =
-                (((page << pshift) | (size_t)(t_new & pmask)) * slot_stride) + (size_t)kvh * D +
-                li * EPL;
-            *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.k_pages_w) + row) =
-                *reinterpret_cast<const uint4*>(knew);
-            *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.v_pages_w) + row) =
-                *reinterpret_cast<const uint4*>(vnew);
+            const uint32_t page = (uint32_t)s_tbl[(t_new >> pshift) - pg0_last];
+            const uint64_t off =
+                (uint64_t)((page << pshift) | (uint32_t)(t_new & pmask)) * slot_bytes + lane_off;
+            Frag<WPL> fk, fv;
+            load_frag(fk, knew);
+            load_frag(fv, vnew);
+            store_frag(reinterpret_cast<char*>(a.k_pages_w) + off, fk);
+            store_frag(reinterpret_cast<char*>(a.v_pages_w) + off, fv);
         }
     }
 
-    // Every stream (wave, lane group) leaves its state in LDS; no cross-lane exchange.
+    // Every stream (wave, 16-lane row) leaves its state in LDS; no cross-lane exchange.
     const int stream = wave * RPI + lg;
 #pragma unroll
     for (int j = 0; j < GH; ++j) {
-        float4* dst = reinterpret_cast<float4*>(s_o + ((size_t)stream * GH + j) * D + li * EPL);
+        float4* dst = reinterpret_cast<float4*>(s_o + stream * SOS + j * D + li * EPL);
 #pragma unroll
         for (int e = 0; e < EPL; e += 4)
             dst[e / 4] = make_float4(o[j][e], o[j][e + 1], o[j][e + 2], o[j][e + 3]);
     }
-    if (li == 0) {
-#pragma unroll
-        for (int j = 0; j < GH; ++j) {
-            s_m[stream * GH + j] = m[j];
-            s_l[stream * GH + j] = l[j];
+    static_for<0, NG>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        constexpr int N = HG::size(g);
+        constexpr int B = HG::base(g);
+        if (is_owner<N>(li)) {
+            const int j = (B + slot_key<N>(li)) * streams + stream;
+            s_m[j] = mr[g];
+            s_t[j] = mt[g];
+            s_l[j] = l[g];
         }
-    }
+    });
     __syncthreads();
 
-    // Merge, phase 1: per (stream, head) the factor f = exp(m_s - M), M the split's maximum.
-    for (int idx = tid; idx < streams * GH; idx += nthreads) {
-        const int j = idx % GH;
-        float M = -INFINITY;
-        for (int s2 = 0; s2 < streams; ++s2) M = fmaxf(M, s_m[s2 * GH + j]);
-        const float ms = (M == -INFINITY) ? 0.f : M;
-        s_f[idx] = fast_exp2(s_m[idx] - ms);
-    }
-    __syncthreads();
-
-    // Merge, phase 2: one weighted sum per output element of the split's partial.
-    for (int idx = tid; idx < GH * D; idx += nthreads) {
-        const int j = idx / D;
-        const int d = idx - j * D;
+    // Merge of the streams: one thread per (head, 4 consecutive elements).  Stream s enters
+    // with the factor exp(m_ref_s - M), M the split's true maximum (at least every stream's
+    // reference, so the factor is at most 1; 0 for a stream that saw no row).  The per-stream
+    // scalars are read four streams at a time.
+    constexpr int D4 = D / 4;
+    for (int idx = tid; idx < GH * D4; idx += nthreads) {
+        const int j = idx / D4;
+        const int c = idx - j * D4;
         if (j >= nh) continue;
-        float O0 = 0.f, O1 = 0.f;
-        int s2 = 0;
-        for (; s2 + 1 < streams; s2 += 2) {
-            O0 = fmaf(s_o[((size_t)s2 * GH + j) * D + d], s_f[s2 * GH + j], O0);
-            O1 = fmaf(s_o[((size_t)(s2 + 1) * GH + j) * D + d], s_f[(s2 + 1) * GH + j], O1);
+        const float4* t4 = reinterpret_cast<const float4*>(s_t + j * streams);
+        const float4* m4 = reinterpret_cast<const float4*>(s_m + j * streams);
+        const float4* l4 = reinterpret_cast<const float4*>(s_l + j * streams);
+        float M = -INFINITY;
+        for (int q = 0; q < nwaves; ++q) {
+            const float4 v = t4[q];
+            M = fmaxf(M, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
         }
-        if (s2 < streams) O0 = fmaf(s_o[((size_t)s2 * GH + j) * D + d], s_f[s2 * GH + j], O0);
-        const size_t slot = ((size_t)b * a.num_q_heads + h0 + j) * S + split;
-        store_partial<FUSED>(a.partial_o + slot * D + d, O0 + O1);
-        if (d == 0) {
-            float L = 0.f, M = -INFINITY;
-            for (int s3 = 0; s3 < streams; ++s3) {
-                L = fmaf(s_l[s3 * GH + j], s_f[s3 * GH + j], L);
-                M = fmaxf(M, s_m[s3 * GH + j]);
+        const float ms = (M == -INFINITY) ? 0.f : M;
+        float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+        float L = 0.f;
+        for (int q = 0; q < nwaves; ++q) {
+            const float4 mq = m4[q];
+            const float4 lq = l4[q];
+            const float f[4] = {fast_exp2(mq.x - ms), fast_exp2(mq.y - ms),
+                                fast_exp2(mq.z - ms), fast_exp2(mq.w - ms)};
+            const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
+            float4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                v[k] = *reinterpret_cast<const float4*>(s_o + (4 * q + k) * SOS + j * D + 4 * c);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                O.x = fmaf(v[k].x, f[k], O.x);
+                O.y = fmaf(v[k].y, f[k], O.y);
+                O.z = fmaf(v[k].z, f[k], O.z);
+                O.w = fmaf(v[k].w, f[k], O.w);
+                L = fmaf(lv[k], f[k], L);
             }
+        }
+        const size_t slot = ((size_t)b * a.num_q_heads + h0 + j) * S + split;
+        float* dst = a.partial_o + slot * D + 4 * c;
+        store_partial<FUSED>(dst + 0, O.x);
+        store_partial<FUSED>(dst + 1, O.y);
+        store_partial<FUSED>(dst + 2, O.z);
+        store_partial<FUSED>(dst + 3, O.w);
+        if (c == 0) {
             store_partial<FUSED>(a.partial_ml + 2 * slot, (L > 0.f) ? M * kLn2 : -INFINITY);
             store_partial<FUSED>(a.partial_ml + 2 * slot + 1, L);
         }
@@ -438,7 +681,7 @@ const void* decode_kernel_ptr() {
 template <typename KV, int D, int GH, bool FUSED>
 hipError_t launch_gh(const DecodeArgs& a, int waves, hipStream_t stream) {
     using G = DecodeGeom<KV, D>;
-    const size_t lds = decode_lds_bytes(waves * G::RPI, GH, D);
+    const size_t lds = decode_lds_bytes(waves * kRowsPerLoad, GH, D);
     // Workgroups asking for more than 64 KB of LDS opt in once per instantiation.
     static size_t opted = 64 * 1024;
     if (lds > opted) {
@@ -466,7 +709,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     // the same bits as the equivalent MHA call.
     const int64_t cap = (int64_t)a.max_pages << a.page_shift;
     const int64_t chunk = (cap + a.num_splits - 1) / a.num_splits;
-    const int64_t rows_per_pass = (int64_t)G::RPI * kWindowRows;
+    const int64_t rows_per_pass = (int64_t)kRowsPerLoad * kWindowRows;
     int waves = (int)std::min<int64_t>(G::kWaves, (chunk + rows_per_pass - 1) / rows_per_pass);
     waves = std::max(waves, 1);
     switch (a.heads_per_wg) {
