@@ -227,15 +227,26 @@ __device__ __forceinline__ float from_owner(float v) {
         return row_bcast<owner_lane<N>(H)>(v);
 }
 
-// A split partial leaves the workgroup by a plain store, or, when another workgroup of the
-// same launch merges it, by a device-scope one (written through this XCD's L2).
-template <bool COHERENT>
-__device__ __forceinline__ void store_partial(float* p, float v) {
-    if constexpr (COHERENT)
-        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-        *p = v;
-}
+// A split partial leaves the workgroup by plain stores, or, when another workgroup of the
+// same launch merges it, by device-scope ones (written through this XCD's L2): 16 bytes of
+// O and 8 bytes of (m, l) per lane, through buffer resources over this workgroup's rows, so
+// that a wave's store covers whole lines rather than a strided scatter of words.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kDeviceScopeStore = 16;  // buffer-instruction cache policy: device scope
+
+struct PartialStore {
+    __amdgpu_buffer_rsrc_t o_rsrc, ml_rsrc;  // over rows [row0, row0 + nh) of the partials
+    __device__ __forceinline__ void o(uint32_t byte_off, float4 v) const {
+        const u32x4 d = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                         __float_as_uint(v.w)};
+        __builtin_amdgcn_raw_buffer_store_b128(d, o_rsrc, byte_off, 0, kDeviceScopeStore);
+    }
+    __device__ __forceinline__ void ml(uint32_t byte_off, float m, float l) const {
+        const u32x2 d = {__float_as_uint(m), __float_as_uint(l)};
+        __builtin_amdgcn_raw_buffer_store_b64(d, ml_rsrc, byte_off, 0, kDeviceScopeStore);
+    }
+};
 
 template <typename KV, int D, int GH, bool FUSED>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
@@ -572,6 +583,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     // reference, so the factor is at most 1; 0 for a stream that saw no row).  The per-stream
     // scalars are read four streams at a time.
     constexpr int D4 = D / 4;
+    PartialStore pst;
+    if constexpr (FUSED) {
+        // Rows of partials of this workgroup's heads: at most 8 heads x 4096 splits x D
+        // floats, far below 2^31 bytes; bases uniform over the workgroup.
+        const size_t row0 = (size_t)b * a.num_q_heads + h0;
+        pst.o_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.partial_o + row0 * S * D, 0,
+                                                       nh * S * D * 4, kRawBufferWord3);
+        pst.ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.partial_ml + row0 * S * 2, 0,
+                                                        nh * S * 8, kRawBufferWord3);
+    }
     for (int idx = tid; idx < GH * D4; idx += nthreads) {
         const int j = idx / D4;
         const int c = idx - j * D4;
@@ -606,15 +627,15 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
                 L = fmaf(lv[k], f[k], L);
             }
         }
-        const size_t slot = ((size_t)b * a.num_q_heads + h0 + j) * S + split;
-        float* dst = a.partial_o + slot * D + 4 * c;
-        store_partial<FUSED>(dst + 0, O.x);
-        store_partial<FUSED>(dst + 1, O.y);
-        store_partial<FUSED>(dst + 2, O.z);
-        store_partial<FUSED>(dst + 3, O.w);
-        if (c == 0) {
-            store_partial<FUSED>(a.partial_ml + 2 * slot, (L > 0.f) ? M * kLn2 : -INFINITY);
-            store_partial<FUSED>(a.partial_ml + 2 * slot + 1, L);
+        const float mo = (L > 0.f) ? M * kLn2 : -INFINITY;
+        if constexpr (FUSED) {
+            const uint32_t js = (uint32_t)(j * S + split);
+            pst.o(js * (uint32_t)(D * 4) + (uint32_t)c * 16u, O);
+            if (c == 0) pst.ml(js * 8u, mo, L);
+        } else {
+            const size_t slot = ((size_t)b * a.num_q_heads + h0 + j) * S + split;
+            reinterpret_cast<float4*>(a.partial_o + slot * D)[c] = O;
+            if (c == 0) reinterpret_cast<float2*>(a.partial_ml)[slot] = make_float2(mo, L);
         }
     }
 
