@@ -81,7 +81,9 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     __shared__ int s_tbl[kTablePages];
     __shared__ float s_m[kWaves][kRows];
     __shared__ float s_l[kWaves][kRows];
-    __shared__ float s_o[kWaves][D][kRows];
+    // Per wave, row and dim; rows padded by one float, so that both the lanes' writes (16
+    // rows x 4 dim groups) and the merge's reads (consecutive dims) hit distinct banks.
+    __shared__ float s_o[kWaves][kRows][D + 1];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
     const int lane = threadIdx.x & 63;
@@ -256,7 +258,7 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
     for (int dt = 0; dt < NC; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_o[wave][NC * (4 * g + i) + dt][c16] = oacc[dt][i];
+        for (int i = 0; i < 4; ++i) s_o[wave][c16][NC * (4 * g + i) + dt] = oacc[dt][i];
     __syncthreads();
 
     for (int idx = threadIdx.x; idx < kRows * D; idx += kWaves * 64) {
@@ -272,7 +274,7 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
         for (int w = 0; w < kWaves; ++w) {
             const float f = fast_exp2(s_m[w][q] - ms);
             L = fmaf(s_l[w][q], f, L);
-            O = fmaf(s_o[w][d][q], f, O);
+            O = fmaf(s_o[w][q][d], f, O);
         }
         a.out[((size_t)(start + r0 + q) * a.num_q_heads + h) * D + d] = (L > 0.f) ? O / L : 0.f;
     }
