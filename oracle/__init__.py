@@ -58,8 +58,12 @@ def _bind(path: str):
     lib.oracle_widen.argtypes = [i, p, ctypes.c_int64, p]
     lib.oracle_widen.restype = None
     lib.oracle_split_range.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.oracle_kv_write_rope.argtypes = [p, p, p, p, i, p, p, p, p, i, p, i, i, i, i, i, i, i, i]
+    lib.oracle_round_to.argtypes = [i, p, ctypes.c_int64, p]
+    lib.oracle_round_to.restype = None
     for name in ("oracle_decode", "oracle_decode_partials", "oracle_combine",
-                 "oracle_prefill", "oracle_kv_write", "oracle_split_range"):
+                 "oracle_prefill", "oracle_kv_write", "oracle_split_range",
+                 "oracle_kv_write_rope"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -95,6 +99,8 @@ MUTANTS = {
     9: "prefill ignores absolute_start",
     10: "page write slot off by one",
     11: "prefill reads page-table row 0 for every segment",
+    12: "RoPE turns pairs the wrong way (sin negated)",
+    13: "RoPE rotates K at position + 1",
 }
 
 
@@ -216,6 +222,37 @@ class Oracle:
         return kp, vp
 
 
+    def kv_write_rope(self, k_new, v_new, k_pages, v_pages, dtype, page_table,
+                      token_table_index, token_position, inv_freq, style, q=None):
+        """Return (K pool, V pool, q) after the page write with rotary position embedding.
+
+        k_new, v_new are f32 [T, Hkv, D]; the pools are copied, not modified; q (f32
+        [T, Hq, D], optional) is returned rotated (a copy), or None."""
+        kp = _pool(k_pages, dtype).copy()
+        vp = _pool(v_pages, dtype).copy()
+        kn, vn = _c(k_new, np.float32), _c(v_new, np.float32)
+        table = _c(page_table, np.int32)
+        owner = _c(token_table_index, np.int32)
+        pos = _c(token_position, np.int32)
+        freq = _c(inv_freq, np.float32)
+        P, ps, Hkv, D = kp.shape
+        qq = None if q is None else np.array(q, dtype=np.float32, order="C", copy=True)
+        hq = 0 if qq is None else qq.shape[1]
+        _check(self._lib.oracle_kv_write_rope(
+            _ptr(kn), _ptr(vn), _ptr(kp), _ptr(vp), DTYPE_CODES[dtype], _ptr(table), _ptr(owner),
+            _ptr(pos), _ptr(freq), int(style), None if qq is None else _ptr(qq), hq,
+            owner.shape[0], table.shape[0], Hkv, D, ps, P, table.shape[1]), "kv_write_rope")
+        return kp, vp, qq
+
+    def round_to(self, values, dtype: str) -> np.ndarray:
+        """f64 values rounded to a pool dtype (through f32, ties to even): float32 values, or
+        uint16 bit patterns for f16 / bf16."""
+        src = _c(values, np.float64)
+        out = np.empty(src.shape, dtype=np.float32 if dtype == "f32" else np.uint16)
+        self._lib.oracle_round_to(DTYPE_CODES[dtype], _ptr(src), src.size, _ptr(out))
+        return out
+
+
 def widen(*a, **k):
     return _load().widen(*a, **k)
 
@@ -242,3 +279,11 @@ def prefill(*a, **k):
 
 def kv_write(*a, **k):
     return _load().kv_write(*a, **k)
+
+
+def kv_write_rope(*a, **k):
+    return _load().kv_write_rope(*a, **k)
+
+
+def round_to(*a, **k):
+    return _load().round_to(*a, **k)

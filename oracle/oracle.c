@@ -355,6 +355,131 @@ int oracle_kv_write(const void* k_new, const void* v_new, void* k_pages, void* v
     return 0;
 }
 
+/* ---------------------------------------------------------------- page write with RoPE */
+
+/* Round x to the nearest value of a binary format with `digits` significant bits, smallest
+ * normal exponent emin (fixed quantum below it: subnormals) and largest finite value
+ * max_finite; ties to even; beyond the overflow threshold, infinity (IEEE 754 rounding).
+ * x / quantum is exact (a power-of-two scaling), and rint rounds half to even. */
+static double round_binary(double x, int digits, int emin, double max_finite) {
+    if (x == 0.0 || isnan(x) || isinf(x)) return x;
+    int e;
+    frexp(x, &e);                       /* |x| in [2^(e-1), 2^e) */
+    int ex = e - 1;
+    if (ex < emin) ex = emin;
+    const double quantum = ldexp(1.0, ex - (digits - 1));
+    const double r = rint(x / quantum) * quantum;
+    if (fabs(r) > max_finite) return copysign(INFINITY, x);
+    return r;
+}
+
+/* Bit pattern of a value already representable in binary16 / bfloat16 (sign, biased
+ * exponent, fraction; exponent 0 for zero and subnormals, all ones for infinity). */
+static uint16_t encode_small(double r, int frac_bits, int bias) {
+    uint16_t sign = signbit(r) ? (uint16_t)(1u << 15) : 0;
+    const double a = fabs(r);
+    const int exp_all_ones = (1 << (15 - frac_bits)) - 1;
+    if (isinf(a)) return sign | (uint16_t)(exp_all_ones << frac_bits);
+    if (a == 0.0) return sign;
+    const double min_normal = ldexp(1.0, 1 - bias);
+    if (a < min_normal) {   /* subnormal: a = frac * 2^(1 - bias - frac_bits) */
+        return sign | (uint16_t)ldexp(a, bias - 1 + frac_bits);
+    }
+    int e;
+    const double f = frexp(a, &e);      /* a = f * 2^e, f in [0.5, 1) */
+    const int biased = e - 1 + bias;
+    const uint32_t frac = (uint32_t)ldexp(2.0 * f - 1.0, frac_bits);
+    return sign | (uint16_t)((biased << frac_bits) | frac);
+}
+
+/* Store f64 value y as element idx of a cache pool: rounded to f32 first (the arithmetic
+ * precision of the kernels, so that both sides round the same f32 value to 16 bits), then
+ * to binary16 or bfloat16, each time to nearest, ties to even. */
+static void store_elem(void* base, int dtype, size_t idx, double y) {
+    const double y32 = round_binary(y, 24, -126, 3.4028234663852886e38);
+    if (dtype == ORACLE_F32) {
+        ((float*)base)[idx] = (float)y32;
+    } else if (dtype == ORACLE_F16) {
+        ((uint16_t*)base)[idx] = encode_small(round_binary(y32, 11, -14, 65504.0), 10, 15);
+    } else {
+        ((uint16_t*)base)[idx] =
+            encode_small(round_binary(y32, 8, -126, 3.3895313892515355e38), 7, 127);
+    }
+}
+
+/* Rotary position embedding of one head row x[0..D) at position pos, in place, in f64.
+ * Pair i (i < D/2) is (2i, 2i+1) for style 0 (adjacent dims) or (i, i + D/2) for style 1
+ * (the two halves): the two pairing conventions the crucible README names as a silent
+ * failure when swapped.  Its angle is the f32 product of f32(pos) and the caller's
+ * frequency inv_freq[i] (the kernels' precision for the angle), and the pair turns by it:
+ * (a, b) -> (a cos t - b sin t, a sin t + b cos t). */
+static void rotate_row(double* x, int head_dim, int pos, const float* inv_freq, int style) {
+    const int half = head_dim / 2;
+    for (int i = 0; i < half; ++i) {
+        const double t = round_binary((double)(float)pos * (double)inv_freq[i], 24, -126,
+                                      3.4028234663852886e38);
+        const double c = cos(t), sn = sin(MUT(12) ? -t : t);
+        const int i0 = style == 0 ? 2 * i : i;
+        const int i1 = style == 0 ? 2 * i + 1 : i + half;
+        const double a = x[i0], b = x[i1];
+        x[i0] = a * c - b * sn;
+        x[i1] = a * sn + b * c;
+    }
+}
+
+/* The page write with RoPE and conversion (crucible results: the K projection writes a
+ * scratch slice, RoPE rotates it, K scatters to the paged pool, V scatters unrotated; the
+ * query is rotated at the same positions before attention):
+ *   q (optional, f32 [T][Hq][D]): rotated in place at token_position[i];
+ *   K pages: rotate(k_new[i]) converted to the pool's dtype at (table[owner][pos / ps],
+ *            pos % ps), as oracle_kv_write places rows;
+ *   V pages: v_new[i] converted, same slot.
+ * A token with a negative position is skipped altogether; one whose owner, position or page
+ * is out of range keeps the pools untouched (its query is still rotated). */
+int oracle_kv_write_rope(const float* k_new, const float* v_new, void* k_pages, void* v_pages,
+                         int dtype, const int32_t* page_table, const int32_t* token_table_index,
+                         const int32_t* token_position, const float* inv_freq, int style,
+                         float* q, int num_q_heads, int num_tokens, int num_tables,
+                         int num_kv_heads, int head_dim, int page_size, int num_pages,
+                         int max_pages_per_seq) {
+    if (num_kv_heads <= 0 || head_dim <= 0 || head_dim % 2 || page_size <= 0) return -1;
+    if (style != 0 && style != 1) return -1;
+    double* row = malloc(sizeof(double) * (size_t)head_dim);
+    if (!row) return -2;
+    for (int i = 0; i < num_tokens; ++i) {
+        const int pos = token_position[i];
+        if (pos < 0) continue;
+        for (int h = 0; q && h < num_q_heads; ++h) {
+            float* qr = q + ((size_t)i * num_q_heads + h) * head_dim;
+            for (int d = 0; d < head_dim; ++d) row[d] = qr[d];
+            rotate_row(row, head_dim, pos, inv_freq, style);
+            for (int d = 0; d < head_dim; ++d) store_elem(qr, ORACLE_F32, (size_t)d, row[d]);
+        }
+        const int owner = token_table_index[i];
+        if (owner < 0 || owner >= num_tables) continue;
+        if (pos >= max_pages_per_seq * page_size) continue;
+        const int page = page_table[(size_t)owner * max_pages_per_seq + pos / page_size];
+        if (page < 0 || page >= num_pages) continue;
+        const size_t slot = (size_t)page * page_size + (size_t)(pos % page_size);
+        for (int h = 0; h < num_kv_heads; ++h) {
+            const size_t src = ((size_t)i * num_kv_heads + h) * head_dim;
+            const size_t dst = (slot * num_kv_heads + h) * head_dim;
+            for (int d = 0; d < head_dim; ++d) row[d] = k_new[src + d];
+            rotate_row(row, head_dim, MUT(13) ? pos + 1 : pos, inv_freq, style);
+            for (int d = 0; d < head_dim; ++d) store_elem(k_pages, dtype, dst + d, row[d]);
+            for (int d = 0; d < head_dim; ++d)
+                store_elem(v_pages, dtype, dst + d, (double)v_new[src + d]);
+        }
+    }
+    free(row);
+    return 0;
+}
+
+/* f64 values rounded to a pool dtype as store_elem does (through f32), for the tests. */
+void oracle_round_to(int dtype, const double* src, int64_t n, void* dst) {
+    for (int64_t i = 0; i < n; ++i) store_elem(dst, dtype, (size_t)i, src[i]);
+}
+
 /* ---------------------------------------------------------------- helpers for the tests */
 
 /* dst[i] = exact f64 value of element i of src (dtype f32, f16 or bf16). */

@@ -51,6 +51,19 @@ int oracle_kv_write(const void* k_new, const void* v_new, void* k_pages, void* v
 
 
 
+/* Page write with rotary position embedding: K rotated at its position, K and V converted
+ * to the pool dtype (through f32, ties to even) and placed as oracle_kv_write places rows;
+ * q (optional) rotated in place.  style 0 pairs dims (2i, 2i+1), style 1 pairs (i, i+D/2). */
+int oracle_kv_write_rope(const float* k_new, const float* v_new, void* k_pages, void* v_pages,
+                         int dtype, const int32_t* page_table, const int32_t* token_table_index,
+                         const int32_t* token_position, const float* inv_freq, int style,
+                         float* q, int num_q_heads, int num_tokens, int num_tables,
+                         int num_kv_heads, int head_dim, int page_size, int num_pages,
+                         int max_pages_per_seq);
+
+/* dst[i] = src[i] rounded to dtype (through f32, to nearest, ties to even). */
+void oracle_round_to(int dtype, const double* src, int64_t n, void* dst);
+
 /* dst[i] = exact f64 value of element i of src. */
 void oracle_widen(int dtype, const void* src, int64_t n, double* dst);
 #endif

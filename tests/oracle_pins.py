@@ -25,6 +25,14 @@ What pins what:
   * causal extent      — the sums of causal positions the crucible results page prints for
                          its benchmark shapes (golden file);
   * page write         — against numpy reshaping of the contiguous rows, byte-exact.
+  * rounding to a pool — against numpy (f32, f16) and torch (bf16) conversions of random
+                         values, and exhaustively: every finite f16 / bf16 pattern rounds to
+                         itself (the encoder is checked against the pinned decoder);
+  * RoPE page write    — closed forms (one pair at angle 1), position 0 is the identity,
+                         the relative-position identity <R(m)q, R(n)k> = <R(m-n)q, k>
+                         (the defining property of rotary embeddings), norm preservation,
+                         the two pairing conventions related by a fixed permutation of dims,
+                         and placement equal to the pinned plain page write at angle 0.
 """
 from __future__ import annotations
 
@@ -457,6 +465,147 @@ def pin_kv_write_skips_invalid(orc):
     assert_bitwise(v, pool, "invalid tokens must not write")
 
 
+def pin_round_to_vs_library(orc):
+    """Rounding f64 values to a pool dtype (through f32, ties to even) equals the library
+    conversions; every finite f16 / bf16 bit pattern rounds to itself."""
+    rng = wl.rng_for(117)
+    vals = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-9, 9, 4000),
+                           [0.0, -0.0, 1.0, 65504.0, 65519.9, 65520.0, 1e6, -1e6, 5.96e-8,
+                            2.98e-8, 1e-45, 3.4e38, -3.5e38, 2.0 ** -24 * 1.5]])
+    with np.errstate(over="ignore"):
+        f32 = vals.astype(np.float32)
+    assert_bitwise(orc.round_to(vals, "f32"), f32, "round to f32")
+    with np.errstate(over="ignore"):
+        assert_bitwise(orc.round_to(vals, "f16"), f32.astype(np.float16).view(np.uint16),
+                       "round to f16")
+    bf = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert_bitwise(orc.round_to(vals, "bf16"), bf, "round to bf16")
+    for dtype in ("f16", "bf16"):
+        bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        w = orc.widen(bits, dtype)
+        keep = ~np.isnan(w)
+        assert_bitwise(orc.round_to(w[keep], dtype), bits[keep], f"{dtype} patterns round to themselves")
+
+
+def _rope_case(rng, T, hkv, d, dtype, ps=4):
+    k_new = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    v_new = rng.standard_normal((T, hkv, d)).astype(np.float32)
+    pages = -(-T // ps) + 1
+    pool = np.full((pages, ps, hkv, d), wl.nan_value(dtype),
+                   dtype=np.float32 if dtype == "f32" else np.uint16)
+    table = rng.permutation(pages)[None, :].astype(np.int32)
+    return k_new, v_new, pool, table
+
+
+def pin_rope_closed_form(orc):
+    """One pair per head, frequency 1: at position 1, (1, 0) turns to (cos 1, sin 1) and
+    (0, 1) to (-sin 1, cos 1); at position 2 by 2 radians; q turns the same way; V does
+    not turn."""
+    k_new = np.array([[[1.0, 0.0], [0.0, 1.0]]] * 2, np.float32)      # [T=2, Hkv=2, D=2]
+    pool = np.zeros((1, 4, 2, 2), np.float32)
+    table = np.zeros((1, 1), np.int32)
+    pos = np.array([1, 2], np.int32)
+    q = k_new.copy()
+    want = np.array([[[math.cos(t), math.sin(t)], [-math.sin(t), math.cos(t)]] for t in (1, 2)])
+    for style in (0, 1):
+        kp, vp, qr = orc.kv_write_rope(k_new, k_new, pool, pool, "f32", table,
+                                       np.zeros(2, np.int32), pos, np.ones(1, np.float32), style,
+                                       q=q)
+        assert_within(kp[0, 1:3].astype(np.float64), want, 1e-7, 0.0, "rope closed form K")
+        assert_within(qr.astype(np.float64), want, 1e-7, 0.0, "rope closed form q")
+        assert_bitwise(vp[0, 1:3], k_new, "V is not rotated")
+
+
+def pin_rope_position_zero(orc):
+    """At position 0 every pair keeps its values: K and V are the converted inputs."""
+    rng = wl.rng_for(118)
+    for dtype in ("f32", "f16", "bf16"):
+        k_new, v_new, pool, table = _rope_case(rng, 1, 3, 64, dtype)
+        freq = (10000.0 ** (-np.arange(32) * 2 / 64)).astype(np.float32)
+        kp, vp, _ = orc.kv_write_rope(k_new, v_new, pool, pool, dtype, table, np.zeros(1, np.int32),
+                                      np.zeros(1, np.int32), freq, 1)
+        page = table[0, 0]
+        assert_bitwise(kp[page, 0], orc.round_to(k_new[0].astype(np.float64), dtype), "pos 0 K")
+        assert_bitwise(vp[page, 0], orc.round_to(v_new[0].astype(np.float64), dtype), "pos 0 V")
+
+
+def pin_rope_relative_position(orc):
+    """<R(m) q, R(n) k> = <R(m - n) q, R(0) k> for every head: the score of a rotated query
+    and key depends on the positions only through m - n.  Frequencies are powers of two and
+    positions small integers, so every angle is exact in f32 and the identity holds to the
+    f32 rounding of the outputs."""
+    rng = wl.rng_for(119)
+    d, hkv = 64, 2
+    freq = (2.0 ** -np.arange(d // 2)).astype(np.float32)
+    for style in (0, 1):
+        for m, n in ((37, 5), (100, 99), (9, 9)):
+            k_new, v_new, pool, _ = _rope_case(rng, 2, hkv, d, "f32")
+            q = rng.standard_normal((2, hkv, d)).astype(np.float32)
+            table = np.arange(pool.shape[0], dtype=np.int32)[None, :]
+            big = np.zeros((200 // 4 + 2, 4, hkv, d), np.float32)
+            tb = np.arange(big.shape[0], dtype=np.int32)[None, :]
+            kk = np.stack([k_new[0], k_new[0]])
+            qq = np.stack([q[0], q[0]])
+            kp, _, qr = orc.kv_write_rope(kk, kk, big, big, "f32", tb, np.zeros(2, np.int32),
+                                          np.array([n, 0], np.int32), freq, style, q=qq)
+            _, _, qr2 = orc.kv_write_rope(kk, kk, big, big, "f32", tb, np.zeros(2, np.int32),
+                                          np.array([m, m - n], np.int32), freq, style, q=qq)
+            lhs = (qr2[0].astype(np.float64) * kp[n // 4, n % 4].astype(np.float64)).sum(-1)
+            rhs = (qr2[1].astype(np.float64) * kp[0, 0].astype(np.float64)).sum(-1)
+            scale = (np.abs(q[0]).astype(np.float64) * np.abs(k_new[0])).sum(-1)
+            assert np.all(np.abs(lhs - rhs) <= 1e-6 * scale), (style, m, n, lhs, rhs)
+
+
+def pin_rope_norm_and_styles(orc):
+    """Each pair keeps its length; pairing (i, i + D/2) equals pairing (2i, 2i + 1) after
+    interleaving the two halves of the row, bit for bit."""
+    rng = wl.rng_for(120)
+    d, hkv, T = 128, 3, 5
+    freq = (10000.0 ** (-np.arange(d // 2) * 2 / d)).astype(np.float32)
+    k_new, v_new, pool, table = _rope_case(rng, T, hkv, d, "f32")
+    q = rng.standard_normal((T, 4, d)).astype(np.float32)
+    perm = np.empty(d, np.int64)
+    perm[0::2] = np.arange(d // 2)
+    perm[1::2] = np.arange(d // 2) + d // 2
+    bigpos = np.array([5, 1234, 40000, 7, 999], np.int32)
+    _, _, qh = orc.kv_write_rope(k_new, v_new, pool, pool, "f32", table, np.full(T, -1, np.int32),
+                                 bigpos, freq, 1, q=q)
+    _, _, qi = orc.kv_write_rope(k_new, v_new, pool, pool, "f32", table, np.full(T, -1, np.int32),
+                                 bigpos, freq, 0, q=q[..., perm])
+    assert_bitwise(qi, qh[..., perm], "halves pairing = adjacent pairing of interleaved halves")
+    a = q.astype(np.float64)
+    b = qh.astype(np.float64)
+    na = a[..., : d // 2] ** 2 + a[..., d // 2:] ** 2
+    nb = b[..., : d // 2] ** 2 + b[..., d // 2:] ** 2
+    assert np.all(np.abs(na - nb) <= 4 * 2.0 ** -23 * na + 1e-30), "pair length kept"
+
+
+def pin_rope_placement_and_skips(orc):
+    """With every frequency 0 (no rotation) the write equals the plain page write of the
+    converted rows, including the tokens it skips; a negative position leaves q alone."""
+    rng = wl.rng_for(121)
+    for dtype in ("bf16", "f16"):
+        hkv, d, ps = 2, 64, 16
+        k_new = rng.standard_normal((5, hkv, d)).astype(np.float32)
+        v_new = rng.standard_normal((5, hkv, d)).astype(np.float32)
+        pool = random_storage(rng, (4, ps, hkv, d), dtype)
+        table = np.array([[2, 0], [1, 9]], np.int32)    # page 9 does not exist
+        owner = np.array([0, 1, 5, -1, 1], np.int32)
+        pos = np.array([3, 17, 0, 0, 5], np.int32)      # 17 -> page 9; owners 5, -1 invalid
+        q = rng.standard_normal((5, 3, d)).astype(np.float32)
+        kp, vp, qr = orc.kv_write_rope(k_new, v_new, pool, pool, dtype, table, owner, pos,
+                                       np.zeros(d // 2, np.float32), 0, q=q)
+        kc = orc.round_to(k_new.astype(np.float64), dtype)
+        vc = orc.round_to(v_new.astype(np.float64), dtype)
+        rk, rv = orc.kv_write(kc, vc, pool, pool, dtype, table, owner, pos)
+        assert_bitwise(kp, rk, "angle 0 == plain write (K)")
+        assert_bitwise(vp, rv, "angle 0 == plain write (V)")
+        assert_bitwise(qr, q, "angle 0 leaves q")
+        _, _, qn = orc.kv_write_rope(k_new, v_new, pool, pool, dtype, table, owner,
+                                     np.full(5, -3, np.int32), np.ones(d // 2, np.float32), 0, q=q)
+        assert_bitwise(qn, q, "negative position: q untouched")
+
+
 # ----------------------------------------------------------------------------- registry
 
 def _golden_rows(name):
@@ -492,5 +641,7 @@ PINS = [
     pin_split_partition, pin_split_combine_equals_unsplit, pin_idle_splits,
     pin_combine_invariances, pin_prefill_vs_sdpa_causal, pin_prefill_rows_equal_decode,
     pin_causality_brute_force, pin_causal_position_counts, pin_kv_write_vs_reshape,
-    pin_kv_write_skips_invalid,
+    pin_kv_write_skips_invalid, pin_round_to_vs_library, pin_rope_closed_form,
+    pin_rope_position_zero, pin_rope_relative_position, pin_rope_norm_and_styles,
+    pin_rope_placement_and_skips,
 ]
