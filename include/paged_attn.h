@@ -3,6 +3,8 @@
  *
  * Operations over a block-paged KV cache:
  *   kv_page_write            scatter new K/V rows into their pages
+ *   kv_page_write_rope       the same, from f32 rows: K (and the query) rotated by RoPE,
+ *                            K and V rounded to the pool dtype
  *   paged_attn_decode        one query row per sequence, split-KV partial softmax
  *   paged_attn_combine       log-sum-exp merge of the split partials
  *   paged_attn_decode_fused  the three above for one decode step, in a single launch
@@ -207,6 +209,39 @@ int kv_page_write(const void* k_new, const void* v_new, void* k_pages, void* v_p
                   const int32_t* token_table_index, const int32_t* token_position,
                   int num_tokens, int num_tables, int num_kv_heads, int head_dim,
                   int page_size, int num_pages, int max_pages_per_seq, void* stream);
+
+/*
+ * Page write with rotary position embedding (crucible, "Paged attention results": the K
+ * projection output is rotated by RoPE and scattered to the paged pool, V is scattered
+ * unrotated, and the query projection is rotated at the same positions before attention;
+ * crucible README, "Validating the forward pass": the two RoPE pairing conventions).
+ * For token i at position p = token_position[i] and each KV head h:
+ *   K[slot][h][:] = rotate(k_new[i][h][:], p) and V[slot][h][:] = v_new[i][h][:], both
+ *   rounded to kv_dtype (to nearest, ties to even), slot as for kv_page_write;
+ *   q[i][hq][:] = rotate(q[i][hq][:], p) in place for every query head, if q is not NULL.
+ * rotate turns pair i (i < head_dim / 2) — dims (2i, 2i+1) for PA_ROPE_ADJACENT, (i,
+ * i + head_dim/2) for PA_ROPE_HALVES — by the angle t = f32(p) * inv_freq[i] (an f32
+ * product): (a, b) -> (a cos t - b sin t, a sin t + b cos t), computed in f32.
+ * A token with p < 0 is skipped altogether.  A token whose owner, position or page id is out
+ * of range writes nothing (its query is still rotated).  Two tokens mapping to the same slot
+ * in one call race (unspecified which one lands).
+ *
+ *   k_new, v_new        [num_tokens][num_kv_heads][head_dim] f32, device (K before RoPE)
+ *   k_pages, v_pages    [num_pages][page_size][num_kv_heads][head_dim] kv_dtype, device
+ *   page_table, token_table_index, token_position   as for kv_page_write
+ *   inv_freq            [head_dim / 2] f32, device: the rotation frequency of each pair, e.g.
+ *                       base^(-2i / head_dim) for a base of 10000
+ *   q                   [num_tokens][num_q_heads][head_dim] f32, device, or NULL
+ * num_tokens == 0 is a valid empty call.
+ */
+typedef enum pa_rope_style { PA_ROPE_ADJACENT = 0, PA_ROPE_HALVES = 1 } pa_rope_style;
+
+int kv_page_write_rope(const float* k_new, const float* v_new, void* k_pages, void* v_pages,
+                       pa_dtype kv_dtype, const int32_t* page_table,
+                       const int32_t* token_table_index, const int32_t* token_position,
+                       const float* inv_freq, pa_rope_style style, float* q, int num_q_heads,
+                       int num_tokens, int num_tables, int num_kv_heads, int head_dim,
+                       int page_size, int num_pages, int max_pages_per_seq, void* stream);
 
 #ifdef __cplusplus
 }

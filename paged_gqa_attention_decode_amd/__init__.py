@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
 
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_ELAUNCH = 0, -1, -2, -3
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_ROPE_ADJACENT, PA_ROPE_HALVES = 0, 1
 
 C_FUNCTIONS = ("paged_attn_status_string", "paged_attn_decode_workspace_bytes",
                "paged_attn_decode", "paged_attn_decode_fused",
                "paged_attn_decode_fused_counters", "paged_attn_combine", "paged_attn_prefill",
-               "kv_page_write")
+               "kv_page_write", "kv_page_write_rope")
 
 
 class PagedAttnError(RuntimeError):
@@ -57,8 +58,10 @@ def raw_library():
         lib.paged_attn_prefill.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, i, i, i, f,
                                            p, p]
         lib.kv_page_write.argtypes = [p, p, p, p, i, p, p, p, i, i, i, i, i, i, i, p]
+        lib.kv_page_write_rope.argtypes = [p, p, p, p, i, p, p, p, p, i, p, i, i, i, i, i, i,
+                                           i, i, p]
         for name in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_combine",
-                     "paged_attn_prefill", "kv_page_write"):
+                     "paged_attn_prefill", "kv_page_write", "kv_page_write_rope"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -242,3 +245,39 @@ def kv_page_write(k_new, v_new, k_pages, v_pages, page_table, token_table_index,
         _dev(token_position, "token_position", torch.int32, 1), T, page_table.shape[0], Hkv,
         D, ps, P, page_table.shape[1], _stream_handle(stream))
     _ok("kv_page_write", rc)
+
+
+def kv_page_write_rope(k_new, v_new, k_pages, v_pages, page_table, token_table_index,
+                       token_position, inv_freq, style=PA_ROPE_HALVES, q=None,
+                       stream=None) -> None:
+    """Rotate k_new [T,Hkv,D] f32 by RoPE at token_position, round K and V to the pool dtype
+    and write them into their (page, slot); rotate q [T,Hq,D] f32 in place if given.
+    inv_freq is [D/2] f32; style PA_ROPE_ADJACENT pairs dims (2i, 2i+1), PA_ROPE_HALVES
+    pairs (i, i + D/2)."""
+    torch = _torch()
+    P, ps, Hkv, D = k_pages.shape
+    T = k_new.shape[0]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (T, Hkv, D) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be [T, Hkv, D] float32")
+    if tuple(v_pages.shape) != tuple(k_pages.shape) or v_pages.dtype != k_pages.dtype:
+        raise ValueError("k_pages / v_pages disagree")
+    if tuple(token_table_index.shape) != (T,) or tuple(token_position.shape) != (T,):
+        raise ValueError("token_table_index and token_position must be [T]")
+    if tuple(inv_freq.shape) != (D // 2,):
+        raise ValueError("inv_freq must be [D/2]")
+    hq = 0
+    if q is not None:
+        if q.dim() != 3 or q.shape[0] != T or q.shape[2] != D:
+            raise ValueError("q must be [T, Hq, D] float32")
+        hq = q.shape[1]
+    rc = raw_library().kv_page_write_rope(
+        _dev(k_new, "k_new", torch.float32, 3), _dev(v_new, "v_new", torch.float32, 3),
+        _dev(k_pages, "k_pages", ndim=4), _dev(v_pages, "v_pages", ndim=4),
+        _kv_dtype(k_pages), _dev(page_table, "page_table", torch.int32, 2),
+        _dev(token_table_index, "token_table_index", torch.int32, 1),
+        _dev(token_position, "token_position", torch.int32, 1),
+        _dev(inv_freq, "inv_freq", torch.float32, 1), int(style),
+        None if q is None else _dev(q, "q", torch.float32, 3), hq, T, page_table.shape[0], Hkv,
+        D, ps, P, page_table.shape[1], _stream_handle(stream))
+    _ok("kv_page_write_rope", rc)

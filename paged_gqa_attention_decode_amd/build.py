@@ -19,7 +19,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpaged_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["api.hip", "decode.hip", "combine.hip", "prefill.hip", "kv_write.hip"]
+SOURCES = ["api.hip", "decode.hip", "combine.hip", "prefill.hip", "kv_write.hip",
+           "kv_write_rope.hip"]
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -272,4 +272,46 @@ int kv_page_write(const void* k_new, const void* v_new, void* k_pages, void* v_p
     return launched(pa::launch_kv_write(a, (hipStream_t)stream));
 }
 
+int kv_page_write_rope(const float* k_new, const float* v_new, void* k_pages, void* v_pages,
+                       pa_dtype kv_dtype, const int32_t* page_table,
+                       const int32_t* token_table_index, const int32_t* token_position,
+                       const float* inv_freq, pa_rope_style style, float* q, int num_q_heads,
+                       int num_tokens, int num_tables, int num_kv_heads, int head_dim,
+                       int page_size, int num_pages, int max_pages_per_seq, void* stream) {
+    if (num_tokens < 0) return PA_EINVAL;
+    if (num_tokens == 0) return PA_OK;
+    if (!k_new || !v_new || !k_pages || !v_pages || !page_table || !token_table_index ||
+        !token_position || !inv_freq)
+        return PA_EINVAL;
+    if (style != PA_ROPE_ADJACENT && style != PA_ROPE_HALVES) return PA_EINVAL;
+    int rc = check_pages(kv_dtype, num_kv_heads, num_kv_heads, head_dim, page_size, num_pages,
+                         max_pages_per_seq);
+    if (rc != PA_OK) return rc;
+    if (num_tables < 1) return PA_EINVAL;
+    if (q && num_q_heads < 1) return PA_EINVAL;
+    if ((int64_t)num_tables * max_pages_per_seq > kI32Max) return PA_EINVAL;
+    const int64_t heads = (int64_t)num_kv_heads + (q ? num_q_heads : 0);
+    if ((int64_t)num_tokens * heads * head_dim > kI32Max * 8LL) return PA_EINVAL;
+    pa::KvRopeArgs a;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_pages = k_pages;
+    a.v_pages = v_pages;
+    a.page_table = page_table;
+    a.token_table_index = token_table_index;
+    a.token_position = token_position;
+    a.inv_freq = inv_freq;
+    a.q = q;
+    a.num_tokens = num_tokens;
+    a.num_tables = num_tables;
+    a.num_kv_heads = num_kv_heads;
+    a.num_q_heads = q ? num_q_heads : 0;
+    a.head_dim = head_dim;
+    a.style = (int)style;
+    a.page_shift = ilog2(page_size);
+    a.num_pages = num_pages;
+    a.max_pages = max_pages_per_seq;
+    return launched(pa::launch_kv_write_rope(a, kv_dtype, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -279,6 +279,20 @@ struct KvWriteArgs {
     int page_shift, num_pages, max_pages;
 };
 
+struct KvRopeArgs {
+    const float* k_new;       // [T][Hkv][D] f32, before the rotation
+    const float* v_new;       // [T][Hkv][D] f32
+    void* k_pages;
+    void* v_pages;
+    const int32_t* page_table;
+    const int32_t* token_table_index;
+    const int32_t* token_position;
+    const float* inv_freq;    // [D/2] rotation frequency of each pair
+    float* q;                 // [T][Hq][D] f32, rotated in place (null: none)
+    int num_tokens, num_tables, num_kv_heads, num_q_heads, head_dim, style;
+    int page_shift, num_pages, max_pages;
+};
+
 // Launchers (one translation unit each).  Return the hipError_t of the launch.
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, bool fused,
                          hipStream_t stream);
@@ -286,5 +300,6 @@ hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t stream
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int q_blocks,
                           hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+hipError_t launch_kv_write_rope(const KvRopeArgs& a, int kv_dtype, hipStream_t stream);
 
 }  // namespace pa

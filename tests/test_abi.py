@@ -29,7 +29,7 @@ def test_header_lists_the_four_entry_points():
     for n in ("paged_attn_decode", "paged_attn_combine", "paged_attn_prefill",
               "kv_page_write", "paged_attn_decode_workspace_bytes",
               "paged_attn_status_string", "paged_attn_decode_fused",
-              "paged_attn_decode_fused_counters"):
+              "paged_attn_decode_fused_counters", "kv_page_write_rope"):
         assert n in names
     assert set(names) == set(pa.C_FUNCTIONS)
 
@@ -189,6 +189,33 @@ def test_kv_write_validation():
     assert call({12: 48}) == pa.PA_EUNSUPPORTED
     assert call({4: -1}) == pa.PA_EINVAL
     assert call({10: 0}) == pa.PA_EINVAL
+
+
+def test_kv_write_rope_validation():
+    w = pa.raw_library().kv_page_write_rope
+    # (k_new, v_new, k_pages, v_pages, dtype, table, owner, pos, inv_freq, style, q, Hq, T,
+    #  ntab, Hkv, D, ps, P, maxp, stream)
+    good = [FAKE, FAKE, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, 1, FAKE, 64, 16, 16, 8, 128, 32,
+            8192, 128, NULL]
+
+    def call(over):
+        args = list(good)
+        for k, v in over.items():
+            args[k] = v
+        return w(*args)
+
+    assert call({12: 0, 0: NULL}) == pa.PA_OK           # no tokens
+    assert call({12: -1}) == pa.PA_EINVAL
+    for i in (0, 1, 2, 3, 5, 6, 7, 8):
+        assert call({i: NULL}) == pa.PA_EINVAL, i
+    assert call({9: 2}) == pa.PA_EINVAL                  # unknown pairing style
+    assert call({9: -1}) == pa.PA_EINVAL
+    assert call({11: 0}) == pa.PA_EINVAL                 # q given without query heads
+    assert call({13: 0}) == pa.PA_EINVAL
+    assert call({15: 96}) == pa.PA_EUNSUPPORTED
+    assert call({16: 48}) == pa.PA_EUNSUPPORTED
+    assert call({4: 7}) == pa.PA_EINVAL
+    assert call({14: 0}) == pa.PA_EINVAL
 
 
 def test_python_binding_rejects_host_tensors():
