@@ -50,8 +50,8 @@ def _bind(path: str):
     p = ctypes.c_void_p
     i = ctypes.c_int
     f = ctypes.c_float
-    lib.oracle_decode.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, f, p]
-    lib.oracle_decode_partials.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, f, i, p, p, p]
+    lib.oracle_decode.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, f, i, p]
+    lib.oracle_decode_partials.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, f, i, i, p, p, p]
     lib.oracle_combine.argtypes = [p, p, p, i, i, i, i, p]
     lib.oracle_prefill.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, i, f, p, p]
     lib.oracle_kv_write.argtypes = [p, p, p, p, i, p, p, p, i, i, i, i, i, i, i]
@@ -101,6 +101,7 @@ MUTANTS = {
     11: "prefill reads page-table row 0 for every segment",
     12: "RoPE turns pairs the wrong way (sin negated)",
     13: "RoPE rotates K at position + 1",
+    14: "sliding window starts one position late",
 }
 
 
@@ -144,8 +145,10 @@ class Oracle:
                "split_range")
         return lo.value, hi.value
 
-    def decode(self, q, k_pages, v_pages, dtype, page_table, context_lens, scale) -> np.ndarray:
-        """Attention of each sequence's single query row over its whole context, f64."""
+    def decode(self, q, k_pages, v_pages, dtype, page_table, context_lens, scale,
+               window=0) -> np.ndarray:
+        """Attention of each sequence's single query row over its whole context (over its
+        last `window` positions when window > 0), f64."""
         q = _c(q, np.float32)
         kp, vp = _pool(k_pages, dtype), _pool(v_pages, dtype)
         table = _c(page_table, np.int32)
@@ -155,10 +158,11 @@ class Oracle:
         out = np.empty((B, Hq, D), dtype=np.float64)
         _check(self._lib.oracle_decode(_ptr(q), _ptr(kp), _ptr(vp), DTYPE_CODES[dtype], _ptr(table),
                                      _ptr(ctx), B, Hq, Hkv, D, ps, table.shape[1],
-                                     float(scale), _ptr(out)), "decode")
+                                     float(scale), int(window), _ptr(out)), "decode")
         return out
 
-    def decode_partials(self, q, k_pages, v_pages, dtype, page_table, context_lens, scale, num_splits):
+    def decode_partials(self, q, k_pages, v_pages, dtype, page_table, context_lens, scale, num_splits,
+                        window=0):
         """Per-split (O [B,Hq,S,D], m [B,Hq,S], l [B,Hq,S]) in natural-log units, f64."""
         q = _c(q, np.float32)
         kp, vp = _pool(k_pages, dtype), _pool(v_pages, dtype)
@@ -172,8 +176,8 @@ class Oracle:
         pl = np.empty((B, Hq, S), dtype=np.float64)
         _check(self._lib.oracle_decode_partials(_ptr(q), _ptr(kp), _ptr(vp), DTYPE_CODES[dtype],
                                               _ptr(table), _ptr(ctx), B, Hq, Hkv, D, ps,
-                                              table.shape[1], float(scale), S, _ptr(po), _ptr(pm),
-                                              _ptr(pl)), "decode_partials")
+                                              table.shape[1], float(scale), int(window), S, _ptr(po),
+                                              _ptr(pm), _ptr(pl)), "decode_partials")
         return po, pm, pl
 
     def combine(self, partial_o, partial_m, partial_l) -> np.ndarray:

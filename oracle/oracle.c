@@ -138,10 +138,18 @@ static int check_heads(int num_q_heads, int num_kv_heads, int head_dim, int page
 
 /* ---------------------------------------------------------------- decode */
 
+/* First attended position of an n-token context under a sliding window of `window`
+ * positions (vllm.cpp PR #383: the windowed arm of the decode kernel): the current token
+ * and the window - 1 before it, [n - window, n); window <= 0 attends the whole context. */
+static int window_start(int n, int window) {
+    if (window <= 0 || n <= window) return 0;
+    return MUT(14) ? n - window + 1 : n - window;
+}
+
 int oracle_decode(const float* q, const void* k_pages, const void* v_pages, int dtype,
                   const int32_t* page_table, const int32_t* context_lens, int num_seqs,
                   int num_q_heads, int num_kv_heads, int head_dim, int page_size,
-                  int max_pages_per_seq, float scale, double* out) {
+                  int max_pages_per_seq, float scale, int window, double* out) {
     if (check_heads(num_q_heads, num_kv_heads, head_dim, page_size)) return -1;
     const int group = num_q_heads / num_kv_heads;
     int max_ctx = 1;
@@ -160,10 +168,12 @@ int oracle_decode(const float* q, const void* k_pages, const void* v_pages, int 
         for (int g = 0; g < num_kv_heads; ++g) {
             gather(k_pages, dtype, row, n, g, num_kv_heads, head_dim, page_size, K);
             gather(v_pages, dtype, row, n, g, num_kv_heads, head_dim, page_size, V);
+            const int w0 = window_start(n, window);
             for (int j = 0; j < group; ++j) {
                 const int h = MUT(5) ? j * num_kv_heads + g : g * group + j;
-                attend(q + ((size_t)b * num_q_heads + h) * head_dim, K, V, n, head_dim,
-                       (double)scale, s, out + ((size_t)b * num_q_heads + h) * head_dim);
+                attend(q + ((size_t)b * num_q_heads + h) * head_dim, K + (size_t)w0 * head_dim,
+                       V + (size_t)w0 * head_dim, n - w0, head_dim, (double)scale, s,
+                       out + ((size_t)b * num_q_heads + h) * head_dim);
             }
         }
     }
@@ -188,8 +198,9 @@ int oracle_split_range(int n, int num_splits, int split, int* lo, int* hi) {
 int oracle_decode_partials(const float* q, const void* k_pages, const void* v_pages, int dtype,
                            const int32_t* page_table, const int32_t* context_lens,
                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                           int page_size, int max_pages_per_seq, float scale, int num_splits,
-                           double* partial_o, double* partial_m, double* partial_l) {
+                           int page_size, int max_pages_per_seq, float scale, int window,
+                           int num_splits, double* partial_o, double* partial_m,
+                           double* partial_l) {
     if (check_heads(num_q_heads, num_kv_heads, head_dim, page_size) || num_splits < 1)
         return -1;
     const int group = num_q_heads / num_kv_heads;
@@ -218,11 +229,15 @@ int oracle_decode_partials(const float* q, const void* k_pages, const void* v_pa
                         dot += (double)qh[d] * K[(size_t)t * head_dim + d];
                     s[t] = (double)scale * dot;
                 }
+                /* The splits partition the attended positions [w0, n). */
+                const int w0 = window_start(n, window);
                 for (int sp = 0; sp < num_splits; ++sp) {
                     size_t slot = ((size_t)b * num_q_heads + h) * num_splits + sp;
                     double* o = partial_o + slot * head_dim;
                     int lo, hi;
-                    oracle_split_range(n, num_splits, sp, &lo, &hi);
+                    oracle_split_range(n - w0, num_splits, sp, &lo, &hi);
+                    lo += w0;
+                    hi += w0;
                     if (lo >= hi) {                       /* idle split */
                         partial_m[slot] = -INFINITY;
                         partial_l[slot] = 0.0;

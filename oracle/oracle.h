@@ -17,18 +17,21 @@ double oracle_bf16_to_f64(uint16_t bits);
 /* [lo, hi) token range of one split of an n-token context (chunk = ceil(n / num_splits)). */
 int oracle_split_range(int n, int num_splits, int split, int* lo, int* hi);
 
-/* out[b][h][d] = attention of q[b][h] over positions 0 .. context_lens[b]-1.  Returns 0. */
+/* out[b][h][d] = attention of q[b][h] over positions 0 .. context_lens[b]-1, or over the
+ * last `window` of them when window > 0.  Returns 0. */
 int oracle_decode(const float* q, const void* k_pages, const void* v_pages, int dtype,
                   const int32_t* page_table, const int32_t* context_lens, int num_seqs,
                   int num_q_heads, int num_kv_heads, int head_dim, int page_size,
-                  int max_pages_per_seq, float scale, double* out);
+                  int max_pages_per_seq, float scale, int window, double* out);
 
-/* Per-split (m, l, unnormalised O) in natural-log units; idle splits (-inf, 0, 0). */
+/* Per-split (m, l, unnormalised O) in natural-log units; idle splits (-inf, 0, 0).  The
+ * splits partition the attended positions (the last `window` when window > 0). */
 int oracle_decode_partials(const float* q, const void* k_pages, const void* v_pages, int dtype,
                            const int32_t* page_table, const int32_t* context_lens,
                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                           int page_size, int max_pages_per_seq, float scale, int num_splits,
-                           double* partial_o, double* partial_m, double* partial_l);
+                           int page_size, int max_pages_per_seq, float scale, int window,
+                           int num_splits, double* partial_o, double* partial_m,
+                           double* partial_l);
 
 /* Log-sum-exp merge of split partials; all-empty rows give zeros. */
 int oracle_combine(const double* partial_o, const double* partial_m, const double* partial_l,

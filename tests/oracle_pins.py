@@ -28,6 +28,10 @@ What pins what:
   * rounding to a pool — against numpy (f32, f16) and torch (bf16) conversions of random
                          values, and exhaustively: every finite f16 / bf16 pattern rounds to
                          itself (the encoder is checked against the pinned decoder);
+  * sliding window     — a window as long as the context changes no bit; windowed decode
+                         equals whole-context decode over only the last rows, placed in a
+                         fresh pool by reshaping (bit-exact), window 1 returns V[ctx-1];
+                         windowed splits + merge equal the unsplit windowed result;
   * RoPE page write    — closed forms (one pair at angle 1), position 0 is the identity,
                          the relative-position identity <R(m)q, R(n)k> = <R(m-n)q, k>
                          (the defining property of rotary embeddings), norm preservation,
@@ -180,6 +184,7 @@ def pin_decode_vs_sdpa(orc):
         (3, 64, 8, 128, 32, "bf16", [64, 31, 129]),
         (1, 12, 12, 64, 1, "f32", [19]),
         (2, 12, 3, 64, 8, "bf16", [17, 40]),
+        (2, 16, 8, 256, 16, "bf16", [33, 200]),       # head_dim 256
     ]
     for batch, hq, hkv, d, ps, dtype, ctxs in cases:
         q, ks, vs, kp, vp, table, ctx = _decode_setup(
@@ -465,6 +470,60 @@ def pin_kv_write_skips_invalid(orc):
     assert_bitwise(v, pool, "invalid tokens must not write")
 
 
+def pin_window_long_is_whole_context(orc):
+    """A window at least as long as the context attends to the whole context: bit-exact
+    equal to no window (window 0)."""
+    rng = wl.rng_for(122)
+    q, ks, vs, kp, vp, table, ctx = _decode_setup(
+        rng, batch=3, hq=8, hkv=2, d=64, ps=16, dtype="f16", ctxs=[40, 1, 300])
+    full = orc.decode(q, kp, vp, "f16", table, ctx, 0.125)
+    for w in (300, 301, 5000):
+        assert_bitwise(orc.decode(q, kp, vp, "f16", table, ctx, 0.125, window=w), full,
+                       f"window {w} >= context")
+
+
+def pin_window_is_last_rows(orc):
+    """Sliding-window decode equals whole-context decode over a sequence made only of the
+    last `window` rows (placed in a fresh pool by reshaping), bit for bit; window 1 returns
+    the last V row exactly."""
+    rng = wl.rng_for(123)
+    ctxs = [300, 57, 1000]
+    q, ks, vs, kp, vp, table, ctx = _decode_setup(
+        rng, batch=3, hq=10, hkv=5, d=128, ps=16, dtype="bf16", ctxs=ctxs)
+    for w in (1, 16, 17, 100):
+        got = orc.decode(q, kp, vp, "bf16", table, ctx, 0.088, window=w)
+        tail_k = [k[max(0, n - w):] for k, n in zip(ks, ctxs)]
+        tail_v = [v[max(0, n - w):] for v, n in zip(vs, ctxs)]
+        tk, tv, tt = build_paged(rng, tail_k, tail_v, 16, "bf16")
+        tctx = np.array([t.shape[0] for t in tail_k], np.int32)
+        want = orc.decode(q, tk, tv, "bf16", tt, tctx, 0.088)
+        assert_bitwise(got, want, f"window {w} == last rows")
+        if w == 1:
+            for b, n in enumerate(ctxs):
+                last = ref_widen(vs[b][n - 1], "bf16")          # [Hkv, D]
+                rep = np.repeat(last, 2, axis=0)                 # group 2
+                assert_bitwise(got[b], rep, "window 1 returns V[ctx-1]")
+
+
+def pin_window_split_combine(orc):
+    """With a window the splits partition the attended positions: split partials plus the
+    merge equal the unsplit windowed result, and splits past the window are idle."""
+    rng = wl.rng_for(124)
+    q, ks, vs, kp, vp, table, ctx = _decode_setup(
+        rng, batch=2, hq=8, hkv=8, d=64, ps=8, dtype="f32", ctxs=[700, 90])
+    for w in (64, 100):
+        full = orc.decode(q, kp, vp, "f32", table, ctx, 0.125, window=w)
+        for sp in (1, 3, 8, 200):
+            po, pm, pl = orc.decode_partials(q, kp, vp, "f32", table, ctx, 0.125, sp, window=w)
+            assert_within(orc.combine(po, pm, pl), full, 1e-12, 1e-12,
+                          f"window {w}, {sp} splits + combine vs unsplit")
+            n_live = (pl > 0).sum(axis=-1)
+            for b, n in enumerate(ctx):
+                attended = min(int(n), w)
+                chunk = -(-attended // sp)
+                assert np.all(n_live[b] == -(-attended // chunk)), (w, sp, b, n_live[b])
+
+
 def pin_round_to_vs_library(orc):
     """Rounding f64 values to a pool dtype (through f32, ties to even) equals the library
     conversions; every finite f16 / bf16 bit pattern rounds to itself."""
@@ -641,7 +700,8 @@ PINS = [
     pin_split_partition, pin_split_combine_equals_unsplit, pin_idle_splits,
     pin_combine_invariances, pin_prefill_vs_sdpa_causal, pin_prefill_rows_equal_decode,
     pin_causality_brute_force, pin_causal_position_counts, pin_kv_write_vs_reshape,
-    pin_kv_write_skips_invalid, pin_round_to_vs_library, pin_rope_closed_form,
+    pin_kv_write_skips_invalid, pin_window_long_is_whole_context, pin_window_is_last_rows,
+    pin_window_split_combine, pin_round_to_vs_library, pin_rope_closed_form,
     pin_rope_position_zero, pin_rope_relative_position, pin_rope_norm_and_styles,
     pin_rope_placement_and_skips,
 ]
