@@ -23,6 +23,8 @@
  *   [minfer-d3-6] minfer step 71 "D3-6 GQA q-head batched attention", 3.2 Excerpts A and F:
  *       the split partition chunk = ceil(nkv / splits), split sp covers
  *       [sp*chunk, min(nkv, (sp+1)*chunk)); idle splits report max = -inf, sum = 0.
+ *   [vllm-cpp-383] vllm.cpp PR #383, "head_dim-128 arm for the warp-split-KV decode kernel":
+ *       the decode kernel's head_dim-256 instantiation and its windowed (HasWindow) arm.
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library allocates
@@ -45,8 +47,10 @@
  *       K/V pages    [num_pages][page_size][Hkv][D]     kv_dtype
  *       page_table   [rows][max_pages_per_seq]          int32, logical page -> physical page
  *     Query head h reads KV head h / (Hq / Hkv).
- *   - Supported: head_dim in {64, 128}; page_size a power of two in [1, 4096];
- *     Hq a multiple of Hkv with Hq / Hkv <= 64; kv_dtype f32, f16 (IEEE binary16) or bf16.
+ *   - Supported: head_dim in {64, 128}, and 256 for decode, the merge and the page writes
+ *     (decode at 256 with f16 or bf16 K/V: [vllm-cpp-383], the head_dim-256 decode arm);
+ *     page_size a power of two in [1, 4096]; Hq a multiple of Hkv with Hq / Hkv <= 64;
+ *     kv_dtype f32, f16 (IEEE binary16) or bf16.
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
@@ -85,8 +89,11 @@ size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int head
  *
  * Sequence b has ctx = context_lens[b] keys, positions 0 .. ctx-1 (ctx counts the current
  * token, whose K/V the caller has already written).  Its token t lives in physical page
- * page_table[b][t / page_size], slot t % page_size.  With chunk = ceil(ctx / num_splits),
- * split s covers tokens [s*chunk, min(ctx, (s+1)*chunk)).  For every query head h and split s:
+ * page_table[b][t / page_size], slot t % page_size.  It attends to positions [w0, ctx):
+ * w0 = 0, or with a sliding window (window > 0; [vllm-cpp-383], the windowed arm of the
+ * decode kernel) w0 = max(0, ctx - window), the current token and the window - 1 before it.
+ * With n = ctx - w0 and chunk = ceil(n / num_splits), split s covers tokens
+ * [w0 + s*chunk, w0 + min(n, (s+1)*chunk)).  For every query head h and split s:
  *     score_t = scale * dot(q[b][h][:], K[t][h / (Hq/Hkv)][:])
  *     m       = max_t score_t                                  (natural-log units)
  *     l       = sum_t exp(score_t - m)
@@ -100,6 +107,7 @@ size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int head
  *   context_lens    [num_seqs] int32, device; 1 <= ctx <= max_pages_per_seq * page_size
  *                   (ctx <= 0 makes every split empty)
  *   scale           normally 1/sqrt(head_dim), rounded to f32 by the caller
+ *   window          sliding window in positions; <= 0 attends the whole context
  *   num_splits      S in [1, 4096]
  *   partial_o       [num_seqs][num_q_heads][S][head_dim] f32, device, written
  *   partial_ml      [num_seqs][num_q_heads][S][2] f32, device, written
@@ -109,8 +117,8 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
                       pa_dtype kv_dtype, const int32_t* page_table,
                       const int32_t* context_lens, int num_seqs, int num_q_heads,
                       int num_kv_heads, int head_dim, int page_size, int num_pages,
-                      int max_pages_per_seq, float scale, int num_splits, float* partial_o,
-                      float* partial_ml, void* stream);
+                      int max_pages_per_seq, float scale, int window, int num_splits,
+                      float* partial_o, float* partial_ml, void* stream);
 
 /*
  * Single-launch decode step: the page write of the current token, the split-KV partials and
@@ -126,9 +134,11 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
  *   k_pages,v_pages written at that one slot per (sequence, KV head), read elsewhere
  *   partial_o, partial_ml  split workspace as for paged_attn_decode (left holding the
  *                   partials)
- *   counters        [num_seqs][num_kv_heads * ceil((Hq/Hkv) / 8)] uint32, device: zero
- *                   before the first call; every call leaves them zero again (the last split
- *                   of a group resets its counter), so the buffer is reused without clearing
+ *   counters        paged_attn_decode_fused_counters(...) uint32, device: zero before the
+ *                   first call; every call leaves them zero again (the last split of a group
+ *                   resets its counter), so the buffer is reused without clearing.  One
+ *                   counter per (sequence, KV head, group of up to 8 query heads, 4 at
+ *                   head_dim 256).
  *   out             [num_seqs][num_q_heads][head_dim] f32, device, written
  * All other arguments and rules as for paged_attn_decode.  Calls that share a counters
  * buffer must not overlap in time (enqueue them on one stream).
@@ -138,10 +148,11 @@ int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new
                             const int32_t* page_table, const int32_t* context_lens,
                             int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                             int page_size, int num_pages, int max_pages_per_seq, float scale,
-                            int num_splits, float* partial_o, float* partial_ml,
+                            int window, int num_splits, float* partial_o, float* partial_ml,
                             uint32_t* counters, float* out, void* stream);
 
-/* Number of uint32 counters paged_attn_decode_fused needs, or 0 for invalid arguments. */
+/* Number of uint32 counters paged_attn_decode_fused needs at any head_dim, or 0 for invalid
+ * arguments: num_seqs * num_kv_heads * 2 * ceil((Hq/Hkv) / 8). */
 size_t paged_attn_decode_fused_counters(int num_seqs, int num_q_heads, int num_kv_heads);
 
 /*

@@ -49,9 +49,10 @@ def raw_library():
         lib.paged_attn_status_string.restype = ctypes.c_char_p
         lib.paged_attn_decode_workspace_bytes.argtypes = [i, i, i, i]
         lib.paged_attn_decode_workspace_bytes.restype = ctypes.c_size_t
-        lib.paged_attn_decode.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, f, i, p, p, p]
+        lib.paged_attn_decode.argtypes = [p, p, p, i, p, p, i, i, i, i, i, i, i, f, i, i, p, p,
+                                          p]
         lib.paged_attn_decode_fused.argtypes = [p, p, p, p, p, i, p, p, i, i, i, i, i, i, i, f,
-                                                i, p, p, p, p, p]
+                                                i, i, p, p, p, p, p]
         lib.paged_attn_decode_fused_counters.argtypes = [i, i, i]
         lib.paged_attn_decode_fused_counters.restype = ctypes.c_size_t
         lib.paged_attn_combine.argtypes = [p, p, i, i, i, i, p, p]
@@ -124,9 +125,10 @@ def _ok(fn, status):
 # ----------------------------------------------------------------------------- entry points
 
 def paged_attn_decode(q, k_pages, v_pages, page_table, context_lens, scale: float,
-                      partial_o, partial_ml, stream=None) -> None:
+                      partial_o, partial_ml, stream=None, window: int = 0) -> None:
     """Split-KV decode partials.  q [B,Hq,D] f32; pages [P,ps,Hkv,D]; page_table [B,maxp]
-    int32; context_lens [B] int32; partial_o [B,Hq,S,D] f32; partial_ml [B,Hq,S,2] f32."""
+    int32; context_lens [B] int32; partial_o [B,Hq,S,D] f32; partial_ml [B,Hq,S,2] f32.
+    window > 0 attends only the last `window` positions of each context."""
     torch = _torch()
     B, Hq, D = q.shape
     P, ps, Hkv, Dk = k_pages.shape
@@ -142,7 +144,8 @@ def paged_attn_decode(q, k_pages, v_pages, page_table, context_lens, scale: floa
         _dev(v_pages, "v_pages", ndim=4), _kv_dtype(k_pages),
         _dev(page_table, "page_table", torch.int32, 2),
         _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D, ps, P,
-        page_table.shape[1], float(scale), S, _dev(partial_o, "partial_o", torch.float32),
+        page_table.shape[1], float(scale), int(window), S,
+        _dev(partial_o, "partial_o", torch.float32),
         _dev(partial_ml, "partial_ml", torch.float32), _stream_handle(stream))
     _ok("paged_attn_decode", rc)
 
@@ -155,11 +158,12 @@ def paged_attn_decode_fused_counters(num_seqs: int, num_q_heads: int,
 
 def paged_attn_decode_fused(q, k_new, v_new, k_pages, v_pages, page_table, context_lens,
                             scale: float, partial_o, partial_ml, counters, out,
-                            stream=None) -> None:
+                            stream=None, window: int = 0) -> None:
     """One-launch decode step: writes the current token (k_new/v_new [B,Hkv,D]) into its
     page, computes the split partials and merges them into out [B,Hq,D] f32.  counters is a
     uint32 buffer (int32 tensor) of paged_attn_decode_fused_counters(...) entries, zero
-    before the first call; each call leaves it zero."""
+    before the first call; each call leaves it zero.  window > 0 attends only the last
+    `window` positions of each context."""
     torch = _torch()
     B, Hq, D = q.shape
     P, ps, Hkv, Dk = k_pages.shape
@@ -182,7 +186,8 @@ def paged_attn_decode_fused(q, k_new, v_new, k_pages, v_pages, page_table, conte
         _dev(v_pages, "v_pages", ndim=4), _kv_dtype(k_pages),
         _dev(page_table, "page_table", torch.int32, 2),
         _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D, ps, P,
-        page_table.shape[1], float(scale), S, _dev(partial_o, "partial_o", torch.float32),
+        page_table.shape[1], float(scale), int(window), S,
+        _dev(partial_o, "partial_o", torch.float32),
         _dev(partial_ml, "partial_ml", torch.float32), _dev(counters, "counters"),
         _dev(out, "out", torch.float32, 3), _stream_handle(stream))
     _ok("paged_attn_decode_fused", rc)

@@ -20,6 +20,10 @@ constexpr int kMaxSplits = 4096;
 constexpr int kMaxGroup = 64;
 constexpr int kMaxHeadsPerWg = 8;
 
+// Query heads one decode workgroup serves: 8, or 4 at head_dim 256 (q and the accumulators
+// of a lane are heads x D/16 floats each).
+int max_heads_per_wg(int head_dim) { return head_dim > 128 ? 4 : kMaxHeadsPerWg; }
+
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int ilog2(int x) {
@@ -34,13 +38,14 @@ int elem_bytes(int d) { return d == PA_F32 ? 4 : 2; }
 
 // Shape checks shared by the calls that read K/V pages.
 int check_pages(int kv_dtype, int num_q_heads, int num_kv_heads, int head_dim, int page_size,
-                int num_pages, int max_pages_per_seq) {
+                int num_pages, int max_pages_per_seq, bool allow_d256 = true) {
     if (!valid_dtype(kv_dtype)) return PA_EINVAL;
     if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0)
         return PA_EINVAL;
     if (head_dim < 1 || page_size < 1 || num_pages < 1 || max_pages_per_seq < 1)
         return PA_EINVAL;
-    if (head_dim != 64 && head_dim != 128) return PA_EUNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128 && !(allow_d256 && head_dim == 256))
+        return PA_EUNSUPPORTED;
     if (!is_pow2(page_size) || page_size > 4096) return PA_EUNSUPPORTED;
     if (num_q_heads / num_kv_heads > kMaxGroup) return PA_EUNSUPPORTED;
     if ((int64_t)max_pages_per_seq * page_size > kI32Max) return PA_EINVAL;
@@ -82,8 +87,8 @@ namespace {
 int make_decode_args(const float* q, const void* k_pages, const void* v_pages, int kv_dtype,
                      const int32_t* page_table, const int32_t* context_lens, int num_seqs,
                      int num_q_heads, int num_kv_heads, int head_dim, int page_size,
-                     int num_pages, int max_pages_per_seq, float scale, int num_splits,
-                     float* partial_o, float* partial_ml, pa::DecodeArgs* out) {
+                     int num_pages, int max_pages_per_seq, float scale, int window,
+                     int num_splits, float* partial_o, float* partial_ml, pa::DecodeArgs* out) {
     if (!q || !k_pages || !v_pages || !page_table || !context_lens || !partial_o || !partial_ml)
         return PA_EINVAL;
     int rc = check_pages(kv_dtype, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
@@ -91,13 +96,16 @@ int make_decode_args(const float* q, const void* k_pages, const void* v_pages, i
     if (rc != PA_OK) return rc;
     if (num_splits < 1) return PA_EINVAL;
     if (num_splits > kMaxSplits) return PA_EUNSUPPORTED;
+    // head_dim 256 is built for 16-bit K/V (an f32 row slice would not fit the registers).
+    if (head_dim == 256 && kv_dtype == PA_F32) return PA_EUNSUPPORTED;
     if (!isfinite(scale)) return PA_EINVAL;
     if (num_seqs > kMaxGridYZ) return PA_EUNSUPPORTED;
     if ((int64_t)num_seqs * max_pages_per_seq > kI32Max ||
         (int64_t)num_seqs * num_q_heads * num_splits * head_dim > kI32Max * 4LL)
         return PA_EINVAL;
     const int group = num_q_heads / num_kv_heads;
-    const int head_groups = (group + kMaxHeadsPerWg - 1) / kMaxHeadsPerWg;
+    const int max_heads = max_heads_per_wg(head_dim);
+    const int head_groups = (group + max_heads - 1) / max_heads;
     const int heads_per_wg = (group + head_groups - 1) / head_groups;
     if ((int64_t)num_kv_heads * head_groups > kMaxGridYZ) return PA_EUNSUPPORTED;
 
@@ -119,6 +127,7 @@ int make_decode_args(const float* q, const void* k_pages, const void* v_pages, i
     a.num_pages = num_pages;
     a.max_pages = max_pages_per_seq;
     a.num_splits = num_splits;
+    a.window = window > 0 ? window : 0;
     a.qscale = scale * pa::kLog2e;
     *out = a;
     return PA_OK;
@@ -132,14 +141,14 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
                       pa_dtype kv_dtype, const int32_t* page_table,
                       const int32_t* context_lens, int num_seqs, int num_q_heads,
                       int num_kv_heads, int head_dim, int page_size, int num_pages,
-                      int max_pages_per_seq, float scale, int num_splits, float* partial_o,
-                      float* partial_ml, void* stream) {
+                      int max_pages_per_seq, float scale, int window, int num_splits,
+                      float* partial_o, float* partial_ml, void* stream) {
     if (num_seqs < 0) return PA_EINVAL;
     if (num_seqs == 0) return PA_OK;
     pa::DecodeArgs a;
     int rc = make_decode_args(q, k_pages, v_pages, kv_dtype, page_table, context_lens, num_seqs,
                               num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
-                              max_pages_per_seq, scale, num_splits, partial_o, partial_ml, &a);
+                              max_pages_per_seq, scale, window, num_splits, partial_o, partial_ml, &a);
     if (rc != PA_OK) return rc;
     return launched(pa::launch_decode(a, kv_dtype, head_dim, false, (hipStream_t)stream));
 }
@@ -149,7 +158,8 @@ size_t paged_attn_decode_fused_counters(int num_seqs, int num_q_heads, int num_k
         return 0;
     const int group = num_q_heads / num_kv_heads;
     const int head_groups = (group + kMaxHeadsPerWg - 1) / kMaxHeadsPerWg;
-    return (size_t)num_seqs * num_kv_heads * head_groups;
+    // Enough for head_dim 256 too (at most 4 heads per workgroup there: twice the groups).
+    return (size_t)num_seqs * num_kv_heads * head_groups * 2;
 }
 
 int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new,
@@ -157,7 +167,7 @@ int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new
                             const int32_t* page_table, const int32_t* context_lens,
                             int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                             int page_size, int num_pages, int max_pages_per_seq, float scale,
-                            int num_splits, float* partial_o, float* partial_ml,
+                            int window, int num_splits, float* partial_o, float* partial_ml,
                             uint32_t* counters, float* out, void* stream) {
     if (num_seqs < 0) return PA_EINVAL;
     if (num_seqs == 0) return PA_OK;
@@ -165,7 +175,7 @@ int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new
     pa::DecodeArgs a;
     int rc = make_decode_args(q, k_pages, v_pages, kv_dtype, page_table, context_lens, num_seqs,
                               num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
-                              max_pages_per_seq, scale, num_splits, partial_o, partial_ml, &a);
+                              max_pages_per_seq, scale, window, num_splits, partial_o, partial_ml, &a);
     if (rc != PA_OK) return rc;
     a.k_new = k_new;
     a.v_new = v_new;
@@ -182,7 +192,7 @@ int paged_attn_combine(const float* partial_o, const float* partial_ml, int num_
     if (num_seqs < 0 || num_q_heads < 1 || num_splits < 1 || head_dim < 1) return PA_EINVAL;
     if (num_seqs == 0) return PA_OK;
     if (!partial_o || !partial_ml || !out) return PA_EINVAL;
-    if (head_dim != 64 && head_dim != 128) return PA_EUNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_EUNSUPPORTED;
     if (num_splits > kMaxSplits) return PA_EUNSUPPORTED;
     if ((int64_t)num_seqs * num_q_heads > kI32Max / 32) return PA_EINVAL;
     pa::CombineArgs a;
@@ -204,7 +214,8 @@ int paged_attn_prefill(const float* q, const void* k_pages, const void* v_pages,
     if (num_segs == 0 || max_chunk_len == 0 || total_tokens == 0) return PA_OK;
     if (!q || !k_pages || !v_pages || !page_table || !seg_desc || !out) return PA_EINVAL;
     int rc = check_pages(kv_dtype, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
-                         max_pages_per_seq);
+                         max_pages_per_seq,
+                         /*allow_d256=*/false);
     if (rc != PA_OK) return rc;
     if (num_tables < 1) return PA_EINVAL;
     if (!isfinite(scale)) return PA_EINVAL;

@@ -34,8 +34,10 @@ hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t stream
     const dim3 grid((a.rows + rpb - 1) / rpb);
     if (head_dim == 64)
         hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, stream, a);
-    else
+    else if (head_dim == 128)
         hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

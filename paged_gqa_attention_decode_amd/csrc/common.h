@@ -243,6 +243,7 @@ struct DecodeArgs {
     float* out;              // [B][Hq][D]
     int num_seqs, num_q_heads, num_kv_heads, group, head_groups, heads_per_wg;
     int page_shift, num_pages, max_pages, num_splits;
+    int window;    // sliding window in positions (0: the whole context)
     float qscale;  // scale * log2(e)
 };
 

@@ -62,9 +62,10 @@ template <typename KV, int D>
 struct DecodeGeom {
     static constexpr int EPL = D / kLanesPerRow;          // elements per lane and row
     static constexpr int WPL = EPL * KV::kBytes / 4;      // 32-bit words per lane and row
-    // Most waves per workgroup: every stream keeps up to 8 heads x D floats in LDS.
-    static constexpr int kWaves = (kStreamLds / (8 * D * 4) / kRowsPerLoad) < kMaxWaves
-                                      ? (kStreamLds / (8 * D * 4) / kRowsPerLoad)
+    static constexpr int kMaxGH = D > 128 ? 4 : 8;        // query heads per workgroup
+    // Most waves per workgroup: every stream keeps up to kMaxGH heads x D floats in LDS.
+    static constexpr int kWaves = (kStreamLds / (kMaxGH * D * 4) / kRowsPerLoad) < kMaxWaves
+                                      ? (kStreamLds / (kMaxGH * D * 4) / kRowsPerLoad)
                                       : kMaxWaves;
 };
 
@@ -325,9 +326,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
             }
         }
     });
+    // The splits partition the attended positions [w0, ctx): the whole context, or with a
+    // sliding window the current token and the window - 1 before it (vllm.cpp PR #383: the
+    // windowed arm of the decode kernel).
     const int S = a.num_splits;
-    const int chunk = (ctx + S - 1) / S;
-    const int lo = min(split * chunk, ctx);
+    const int w0 = (a.window > 0 && ctx > a.window) ? ctx - a.window : 0;
+    const int n_att = ctx - w0;
+    const int chunk = (n_att + S - 1) / S;
+    const int lo = w0 + min(split * chunk, n_att);
     const int hi = min(lo + chunk, ctx);
     if (whole_row) {
 #pragma unroll
@@ -728,7 +734,8 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     // the split size, head_dim and dtype, never on the batch or the head grouping, so a
     // sequence's result is bit-identical whatever it is batched with, and a GQA group gives
     // the same bits as the equivalent MHA call.
-    const int64_t cap = (int64_t)a.max_pages << a.page_shift;
+    int64_t cap = (int64_t)a.max_pages << a.page_shift;
+    if (a.window > 0 && a.window < cap) cap = a.window;  // positions attended at most
     const int64_t chunk = (cap + a.num_splits - 1) / a.num_splits;
     const int64_t rows_per_pass = (int64_t)kRowsPerLoad * kWindowRows;
     int waves = (int)std::min<int64_t>(G::kWaves, (chunk + rows_per_pass - 1) / rows_per_pass);
@@ -738,16 +745,27 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
         case 2: return launch_gh<KV, D, 2, FUSED>(a, waves, stream);
         case 3: return launch_gh<KV, D, 3, FUSED>(a, waves, stream);
         case 4: return launch_gh<KV, D, 4, FUSED>(a, waves, stream);
-        case 5: return launch_gh<KV, D, 5, FUSED>(a, waves, stream);
-        case 6: return launch_gh<KV, D, 6, FUSED>(a, waves, stream);
-        case 7: return launch_gh<KV, D, 7, FUSED>(a, waves, stream);
-        case 8: return launch_gh<KV, D, 8, FUSED>(a, waves, stream);
-        default: return hipErrorInvalidValue;
+        default: break;
     }
+    if constexpr (G::kMaxGH == 8) {
+        switch (a.heads_per_wg) {
+            case 5: return launch_gh<KV, D, 5, FUSED>(a, waves, stream);
+            case 6: return launch_gh<KV, D, 6, FUSED>(a, waves, stream);
+            case 7: return launch_gh<KV, D, 7, FUSED>(a, waves, stream);
+            case 8: return launch_gh<KV, D, 8, FUSED>(a, waves, stream);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 template <bool FUSED>
 hipError_t launch_all(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
+    if (head_dim == 256) {  // 16-bit K/V only
+        if (kv_dtype == 1) return launch_typed<F16, 256, FUSED>(a, stream);
+        if (kv_dtype == 2) return launch_typed<BF16, 256, FUSED>(a, stream);
+        return hipErrorInvalidValue;
+    }
     if (head_dim == 64) {
         if (kv_dtype == 0) return launch_typed<F32, 64, FUSED>(a, stream);
         if (kv_dtype == 1) return launch_typed<F16, 64, FUSED>(a, stream);

@@ -79,7 +79,7 @@ def rng_for(case_id) -> np.random.Generator:
 
 
 def named_rng(index: int) -> np.random.Generator:
-    ss = np.random.SeedSequence(MASTER_SEED).spawn(5)[index]
+    ss = np.random.SeedSequence(MASTER_SEED).spawn(7)[index]   # child i does not depend on n
     return np.random.Generator(np.random.PCG64(ss))
 
 
@@ -105,6 +105,7 @@ class Workload:
     layers: int = 1            # layers per model step (decode step = all layers)
     scale: float = 0.0         # 0: 1/sqrt(head_dim) rounded to f32
     rotations: int = 1         # disjoint page sets the bench cycles through
+    window: int = 0            # decode: sliding window in positions (0: whole context)
     description: str = ""
 
     @property
@@ -139,6 +140,17 @@ WORKLOADS = {
         hkv=8, head_dim=128, page_size=32, dtype="bf16", batch=16, ctx_range=(64, 4096),
         num_pages=8192, num_splits=8, rotations=6,
         description="continuous-batching decode, 16 sequences in a shared 8192-page pool"),
+    # Measurement shapes for the windowed and head_dim-256 decode arms (vllm.cpp PR #383
+    # names the arms; it fixes no model shape for them): synthetic, same recipe.
+    "decode_b16_hq64_hkv8_d128_ctx64to4096_w1024_bf16": Workload(
+        name="decode_b16_hq64_hkv8_d128_ctx64to4096_w1024_bf16", kind="decode", index=5,
+        hq=64, hkv=8, head_dim=128, page_size=32, dtype="bf16", batch=16, ctx_range=(64, 4096),
+        num_pages=8192, num_splits=8, rotations=6, window=1024,
+        description="the continuous-batching decode with a 1024-position sliding window"),
+    "decode_hq16_hkv8_d256_ctx4096_bf16": Workload(
+        name="decode_hq16_hkv8_d256_ctx4096_bf16", kind="decode", index=6, hq=16, hkv=8,
+        head_dim=256, page_size=16, dtype="bf16", ctx=(4096,), num_pages=256, num_splits=32,
+        layers=16, description="head_dim-256 decode, batch 1, 16 layers per step"),
 }
 
 
@@ -159,6 +171,7 @@ class DecodeCase:
     scale: float
     num_splits: int
     extra_tables: list = field(default_factory=list)  # other rotations' tables
+    window: int = 0            # sliding window in positions (0: whole context)
 
     @property
     def shape(self):
@@ -171,9 +184,10 @@ class DecodeCase:
 def make_decode_case(rng: np.random.Generator, *, batch, hq, hkv, head_dim, page_size, dtype,
                      ctx=None, ctx_range=None, num_pages=0, max_pages_per_seq=0,
                      num_splits=1, scale=None, poison=True, rotations=1,
-                     new_token_in_pool=False) -> DecodeCase:
+                     new_token_in_pool=False, window=0) -> DecodeCase:
     """Draw one decode case.  The current token (position ctx-1) of every sequence arrives
-    in k_new/v_new; its pool slot is poisoned unless ``new_token_in_pool``."""
+    in k_new/v_new; its pool slot is poisoned unless ``new_token_in_pool``.  With a sliding
+    window, the positions before it are poisoned too (no decode may read them)."""
     q = rng.standard_normal((batch, hq, head_dim), dtype=np.float32)
     if ctx is not None:
         ctx_arr = np.broadcast_to(np.asarray(ctx, dtype=np.int64), (batch,)).copy()
@@ -220,24 +234,26 @@ def make_decode_case(rng: np.random.Generator, *, batch, hq, hkv, head_dim, page
             v_pages[p, pos[b] % page_size] = v_new[b]
     if poison:
         _poison_decode(k_pages, v_pages, table, ctx32, dtype,
-                       keep_current=new_token_in_pool)
+                       keep_current=new_token_in_pool, window=window)
     return DecodeCase(q=q, k_pages=k_pages, v_pages=v_pages, page_table=table,
                       context_lens=ctx32, k_new=k_new, v_new=v_new,
                       token_table_index=np.arange(batch, dtype=np.int32), token_position=pos,
                       dtype=dtype,
                       scale=float(np.float32(scale if scale else 1.0 / math.sqrt(head_dim))),
-                      num_splits=num_splits, extra_tables=tables[1:])
+                      num_splits=num_splits, extra_tables=tables[1:], window=int(window))
 
 
-def _poison_decode(k_pages, v_pages, table, ctx, dtype, keep_current):
-    """NaN into every pool byte no decode of these sequences may read."""
+def _poison_decode(k_pages, v_pages, table, ctx, dtype, keep_current, window=0):
+    """NaN into every pool byte no decode of these sequences may read: unowned pages, slots
+    past the last position, the current token's slot unless it is kept, and positions
+    before a sliding window."""
     num_pages, ps = k_pages.shape[:2]
     live = np.zeros((num_pages, ps), dtype=bool)
     for b in range(table.shape[0]):
         n = int(ctx[b]) if keep_current else int(ctx[b]) - 1
-        for t in range(0, n, ps):
-            page = table[b, t // ps]
-            live[page, : min(ps, n - t)] = True
+        t0 = max(0, int(ctx[b]) - window) if window > 0 else 0
+        for t in range(t0, n):
+            live[table[b, t // ps], t % ps] = True
     nan = nan_value(dtype)
     k_pages[~live] = nan
     v_pages[~live] = nan
@@ -251,7 +267,7 @@ def workload_decode_case(w: Workload, poison=True, new_token_in_pool=False) -> D
         rng, batch=w.batch, hq=w.hq, hkv=w.hkv, head_dim=w.head_dim, page_size=w.page_size,
         dtype=w.dtype, ctx=w.ctx if w.ctx else None, ctx_range=w.ctx_range or None,
         num_pages=w.num_pages, num_splits=w.num_splits, scale=w.attn_scale, poison=poison,
-        rotations=w.rotations, new_token_in_pool=new_token_in_pool)
+        rotations=w.rotations, new_token_in_pool=new_token_in_pool, window=w.window)
 
 
 # --------------------------------------------------------------------------- prefill cases

@@ -39,9 +39,10 @@ def host(t: torch.Tensor) -> np.ndarray:
 class DecodeRun:
     """Device copies of a DecodeCase plus workspace; `step` runs write -> decode -> combine."""
 
-    def __init__(self, case, num_splits=None):
+    def __init__(self, case, num_splits=None, window=None):
         self.case = case
         self.S = int(num_splits or case.num_splits)
+        self.window = int(case.window if window is None else window)
         dt = case.dtype
         self.q = dev(case.q)
         self.kp = dev(case.k_pages, dt)
@@ -63,7 +64,7 @@ class DecodeRun:
 
     def decode(self):
         pa.paged_attn_decode(self.q, self.kp, self.vp, self.table, self.ctx, self.case.scale,
-                             self.po, self.pml)
+                             self.po, self.pml, window=self.window)
         pa.paged_attn_combine(self.po, self.pml, self.out)
 
     def step(self):
@@ -80,6 +81,6 @@ class DecodeRun:
             self.counters = torch.zeros(n, dtype=torch.int32, device=DEV)
         pa.paged_attn_decode_fused(self.q, self.k_new, self.v_new, self.kp, self.vp, self.table,
                                    self.ctx, self.case.scale, self.po, self.pml, self.counters,
-                                   self.out)
+                                   self.out, window=self.window)
         torch.cuda.synchronize()
         return host(self.out)

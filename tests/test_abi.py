@@ -60,16 +60,19 @@ def test_workspace_bytes():
     assert pa.paged_attn_decode_workspace_bytes(1, 40, 128, 0) == 0
 
 
-# decode(q, k, v, dtype, table, ctx, B, Hq, Hkv, D, ps, P, maxp, scale, S, po, pml, stream)
+# decode(q, k, v, dtype, table, ctx, B, Hq, Hkv, D, ps, P, maxp, scale, window, S, po, pml,
+#        stream)
 GOOD_DECODE = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, table=FAKE, ctx=FAKE, B=1, Hq=40, Hkv=8,
-                   D=128, ps=16, P=204, maxp=204, scale=0.0884, S=32, po=FAKE, pml=FAKE)
+                   D=128, ps=16, P=204, maxp=204, scale=0.0884, window=0, S=32, po=FAKE,
+                   pml=FAKE)
 
 
 def decode(**kw):
     a = dict(GOOD_DECODE, **kw)
     return pa.raw_library().paged_attn_decode(
         a["q"], a["k"], a["v"], a["dtype"], a["table"], a["ctx"], a["B"], a["Hq"], a["Hkv"],
-        a["D"], a["ps"], a["P"], a["maxp"], a["scale"], a["S"], a["po"], a["pml"], NULL)
+        a["D"], a["ps"], a["P"], a["maxp"], a["scale"], a["window"], a["S"], a["po"], a["pml"],
+        NULL)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -85,6 +88,9 @@ def decode(**kw):
     (dict(Hq=41), pa.PA_EINVAL),
     (dict(Hkv=0), pa.PA_EINVAL),
     (dict(D=96), pa.PA_EUNSUPPORTED),
+    (dict(D=256, dtype=0), pa.PA_EUNSUPPORTED),     # head_dim 256 is built for 16-bit K/V
+    (dict(D=512), pa.PA_EUNSUPPORTED),
+    (dict(D=256, q=NULL), pa.PA_EINVAL),
     (dict(D=0), pa.PA_EINVAL),
     (dict(ps=12), pa.PA_EUNSUPPORTED),
     (dict(ps=0), pa.PA_EINVAL),
@@ -105,15 +111,17 @@ def test_decode_validation(kw, status):
 
 def test_fused_counters_and_validation():
     lib = pa.raw_library()
-    assert pa.paged_attn_decode_fused_counters(1, 40, 8) == 8
-    assert pa.paged_attn_decode_fused_counters(16, 64, 8) == 128
-    assert pa.paged_attn_decode_fused_counters(2, 12 * 16, 12) == 2 * 12 * 2   # G=16: 2 groups
+    # one per (sequence, KV head, group of 8 query heads), doubled to cover head_dim 256
+    # (groups of 4 there)
+    assert pa.paged_attn_decode_fused_counters(1, 40, 8) == 8 * 2
+    assert pa.paged_attn_decode_fused_counters(16, 64, 8) == 128 * 2
+    assert pa.paged_attn_decode_fused_counters(2, 12 * 16, 12) == 2 * 12 * 2 * 2   # G=16
     assert pa.paged_attn_decode_fused_counters(1, 41, 8) == 0
     f = lib.paged_attn_decode_fused
-    # (q, k_new, v_new, kp, vp, dtype, table, ctx, B, Hq, Hkv, D, ps, P, maxp, scale, S,
-    #  po, pml, counters, out, stream)
+    # (q, k_new, v_new, kp, vp, dtype, table, ctx, B, Hq, Hkv, D, ps, P, maxp, scale, window,
+    #  S, po, pml, counters, out, stream)
     good = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, 40, 8, 128, 16, 204, 204, 0.0884,
-            32, FAKE, FAKE, FAKE, FAKE, NULL]
+            0, 32, FAKE, FAKE, FAKE, FAKE, NULL]
 
     def call(over):
         args = list(good)
@@ -122,10 +130,11 @@ def test_fused_counters_and_validation():
         return f(*args)
 
     assert call({8: 0, 0: NULL}) == pa.PA_OK
-    for i in (0, 1, 2, 3, 4, 6, 7, 17, 18, 19, 20):
+    for i in (0, 1, 2, 3, 4, 6, 7, 18, 19, 20, 21):
         assert call({i: NULL}) == pa.PA_EINVAL, i
     assert call({11: 96}) == pa.PA_EUNSUPPORTED
-    assert call({16: 0}) == pa.PA_EINVAL
+    assert call({11: 256, 5: 0}) == pa.PA_EUNSUPPORTED
+    assert call({17: 0}) == pa.PA_EINVAL
     assert call({9: 41}) == pa.PA_EINVAL
 
 
@@ -162,6 +171,7 @@ def test_prefill_validation():
     assert call({6: -1}) == pa.PA_EINVAL
     assert call({10: 13}) == pa.PA_EINVAL               # 13 % 12
     assert call({12: 80}) == pa.PA_EUNSUPPORTED
+    assert call({12: 256}) == pa.PA_EUNSUPPORTED        # head_dim 256: decode only
     assert call({13: 24}) == pa.PA_EUNSUPPORTED
     assert call({3: 3}) == pa.PA_EINVAL
     assert call({16: math.nan}) == pa.PA_EINVAL
@@ -185,7 +195,8 @@ def test_kv_write_validation():
     for i in (0, 1, 2, 3, 5, 6, 7):
         assert call({i: NULL}) == pa.PA_EINVAL, i
     assert call({9: 0}) == pa.PA_EINVAL
-    assert call({11: 256}) == pa.PA_EUNSUPPORTED
+    assert call({11: 512}) == pa.PA_EUNSUPPORTED
+    assert call({11: 96}) == pa.PA_EUNSUPPORTED
     assert call({12: 48}) == pa.PA_EUNSUPPORTED
     assert call({4: -1}) == pa.PA_EINVAL
     assert call({10: 0}) == pa.PA_EINVAL

@@ -26,7 +26,7 @@ def oracle_step(case):
     kp, vp = oracle.kv_write(case.k_new, case.v_new, case.k_pages, case.v_pages, case.dtype,
                              case.page_table, case.token_table_index, case.token_position)
     out = oracle.decode(case.q, kp, vp, case.dtype, case.page_table, case.context_lens,
-                        case.scale)
+                        case.scale, window=case.window)
     return kp, vp, out
 
 
@@ -34,7 +34,8 @@ def check_partials(run, case, kp, vp):
     po = host(run.po).astype(np.float64)
     pml = host(run.pml).astype(np.float64)
     ro, rm, rl = oracle.decode_partials(case.q, kp, vp, case.dtype, case.page_table,
-                                        case.context_lens, case.scale, run.S)
+                                        case.context_lens, case.scale, run.S,
+                                        window=run.window)
     m, l = pml[..., 0], pml[..., 1]
     idle = rl == 0
     assert np.array_equal(l == 0, idle), "idle-split pattern differs"
