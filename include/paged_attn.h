@@ -183,6 +183,11 @@ int paged_attn_combine(const float* partial_o, const float* partial_ml, int num_
  * an infinity or NaN held at a later position of the same chunk.
  * Segments must not overlap in the packed dimension; rows not covered by any segment are
  * left untouched.
+ * Arithmetic: f32 products and sums for an f32 pool.  For an f16/bf16 pool the products run
+ * on the 16-bit matrix units with f32 accumulation: K and V enter unchanged, while the
+ * scaled q and the softmax weights are each carried as two 16-bit terms (hi + lo, residual
+ * below 2^-16 of the value for bf16, 2^-22 for f16), so the result stays close to f32
+ * rounding rather than to one 16-bit rounding of q and of the weights.
  *
  *   q               [total_tokens][num_q_heads][head_dim] f32, device
  *   k_pages,v_pages [num_pages][page_size][num_kv_heads][head_dim] kv_dtype, device

@@ -1,4 +1,4 @@
-// prefill.hip — causal packed prefill over segment descriptors, f32 MFMA.
+// prefill.hip — causal packed prefill over segment descriptors on the MFMA units.
 //
 // Method (crucible, "Paged attention results": descriptors {packed_start, chunk_len,
 // absolute_start, table_index}; a tile never crosses request ownership; a packed row at
@@ -18,64 +18,259 @@
 //         the 8 waves, starting at a block-dependent wave; the 8 partial softmax states
 //         merge through LDS at the end.  The page ids of the block's key range are staged in
 //         LDS, 1024 at a time.
-//   math  v_mfma_f32_16x16x4_f32.  Scores are computed transposed, S^T = K * Q^T (16 keys x
-//         16 rows per MFMA), so each lane ends with 4 keys of ONE query row (row = lane % 16).
-//         That register layout is exactly the B operand P^T of O^T += V^T * P^T, so the
-//         probabilities never leave registers, and the O^T accumulator also keeps one query
-//         row per lane: row max, rescale and sum stay lane-local except for one max over the
-//         4 lane groups per tile.
-//   data  K rows are read 4 consecutive dims per lane (16 B for f32).  The PV product takes
-//         its output dims in the order d = NC * c + dt (c the accumulator row, dt the
-//         16-dim block), so the V operands a lane needs for one key are NC consecutive
-//         dims: one 16-byte load per key for D = 64.  Keys past the block's last visible
-//         position are clamped onto it (no branch around a load) and given zero V; keys past a
-//         row's own position are masked to -inf before the exponential.  Q is pre-scaled by
-//         scale*log2(e).
+//   math  Scores are computed transposed, S^T = K * Q^T (16 keys x 16 rows per MFMA), so
+//         each lane ends with 4 keys of ONE query row (row = lane % 16).  That register
+//         layout is the B operand P^T of O^T += V^T * P^T, so the probabilities never leave
+//         registers, and the O^T accumulator also keeps one query row per lane: row max,
+//         rescale and sum stay lane-local except for one max over the 4 lane groups per
+//         tile.  Q is pre-scaled by scale*log2(e).  Two operand sets share this frame:
+//         - f32 K/V: v_mfma_f32_16x16x4_f32.  K rows are read 4 consecutive dims per lane
+//           (16 B).  The PV product takes its output dims in the order d = NC * c + dt (c
+//           the accumulator row, dt the 16-dim block), so the V operands a lane needs for
+//           one key are NC consecutive dims: one 16-byte load per key for D = 64.
+//         - f16/bf16 K/V: v_mfma_f32_16x16x32_{f16,bf16}, K and V straight from the pool.
+//           The f32 operands Q and P are each split into two terms of the pool's 16-bit
+//           type, x = hi + lo, and both terms are multiplied (K q_hi + K q_lo, V p_hi +
+//           V p_lo): the residual of the split is below 2^-16 |x| for bf16 and 2^-22 |x|
+//           for f16, where one rounding of Q and P to bf16 alone (2^-9 |x|) can exceed the
+//           16-bit tolerance on standard-normal inputs.  A lane's 8 K elements of one MFMA
+//           are 8 consecutive dims (one 16-byte load).  For PV the contraction runs over
+//           keys; the MFMA pairs A's and B's k index through the same (lane group, element)
+//           slot, so the keys are assigned to slots as the score layout already holds them:
+//           element e of lane group g is key 16 (e / 4) + 4 g + e % 4, and P^T is the lane's
+//           own 8 probabilities.  V is loaded as NC consecutive dims of each of those 8 keys
+//           (8 or 16 bytes per key) and regrouped into per-dim-block operands by byte
+//           permutes.
+//   keys  Keys past the block's last visible position are clamped onto it (no branch around
+//         a load); keys past a row's own position are masked to -inf before the
+//         exponential, so their weight is exactly zero.
 #include "common.h"
 
 namespace pa {
 namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ floatx4 mfma16(float a, float b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Four consecutive elements starting at p, widened to f32.
-template <typename KV>
-__device__ __forceinline__ void load4(const typename KV::storage* p, float* out) {
-    if constexpr (KV::kBytes == 4) {
-        const float4 t = *reinterpret_cast<const float4*>(p);
-        out[0] = t.x;
-        out[1] = t.y;
-        out[2] = t.z;
-        out[3] = t.w;
-    } else {
-        const uint2 t = *reinterpret_cast<const uint2*>(p);
-        widen_word(KV{}, t.x, out);
-        widen_word(KV{}, t.y, out + 2);
-    }
-}
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 8;
 constexpr int kRows = 16;         // query rows per workgroup
 constexpr int kTileKeys = 32;     // keys per wave per step (two 16-key MFMA blocks)
 constexpr int kTablePages = 1024; // page ids staged in LDS per slice of the key range
 
-// One wave's operands for one 32-key tile.
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma32(F16, uint4 a, uint4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a),
+                                                   __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma32(BF16, uint4 a, uint4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// x and y each split into hi + lo terms of the 16-bit type (both rounded to nearest even):
+// hi packs (hi(x), hi(y)) and lo packs (lo(x), lo(y)), x in the low half.
+__device__ __forceinline__ void split_pair(F16, float x, float y, uint32_t& hi, uint32_t& lo) {
+    const _Float16 hx = (_Float16)x, hy = (_Float16)y;
+    const _Float16 lx = (_Float16)(x - (float)hx), ly = (_Float16)(y - (float)hy);
+    hi = (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+    lo = (uint32_t)__builtin_bit_cast(uint16_t, lx) | ((uint32_t)__builtin_bit_cast(uint16_t, ly) << 16);
+}
+__device__ __forceinline__ void split_pair(BF16, float x, float y, uint32_t& hi, uint32_t& lo) {
+    const __bf16 hx = (__bf16)x, hy = (__bf16)y;
+    const __bf16 lx = (__bf16)(x - (float)hx), ly = (__bf16)(y - (float)hy);
+    hi = (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
+    lo = (uint32_t)__builtin_bit_cast(uint16_t, lx) | ((uint32_t)__builtin_bit_cast(uint16_t, ly) << 16);
+}
+
+// The 16-bit element sel of word a (low half) and of word b (high half), sel 0 or 1.
+__device__ __forceinline__ uint32_t pair_halves(uint32_t a, uint32_t b, int sel) {
+    return __builtin_amdgcn_perm(b, a, sel ? 0x07060302u : 0x05040100u);
+}
+
+// Operands and tile products of one wave.  `row_off(key)` gives a key's element offset
+// within the pool (page translated); kp and vp point at the kv head's dims of slot 0.
+template <typename KV, int D>
+struct Operands;
+
+// f32 K/V on v_mfma_f32_16x16x4_f32.
 template <int D>
-struct PrefillTile {
-    // K operand: lane (g, c16) of block st holds K[j0 + 16 st + c16][16c + 4g + kk].
-    float kf[2][D / 16][4];
-    // V^T operand of MFMA (st, i, dt): lane (g, c16) holds V[j0 + 16 st + 4g + i][NC c16 + dt].
-    float vf[2][4][D / 16];
+struct Operands<F32, D> {
+    static constexpr int NC = D / 16;
+    // Q^T operand: lane (g, c16) holds Q[row][16c + 4g + kk], kk = 0..3.
+    float q[NC][4];
+    struct Tile {
+        // K operand: lane (g, c16) of block st holds K[j0 + 16 st + c16][16c + 4g + kk].
+        float kf[2][NC][4];
+        // V^T operand of MFMA (st, i, dt): lane (g, c16) holds V[j0 + 16 st + 4g + i][NC c16 + dt].
+        float vf[2][4][NC];
+    };
+
+    __device__ __forceinline__ void load_q(const float* row, float qs, int g) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float4 t = *reinterpret_cast<const float4*>(row + 16 * c + 4 * g);
+            q[c][0] = t.x * qs;
+            q[c][1] = t.y * qs;
+            q[c][2] = t.z * qs;
+            q[c][3] = t.w * qs;
+        }
+    }
+
+    template <class RowOff>
+    __device__ __forceinline__ static void load_tile(Tile& tl, const float* kp, const float* vp,
+                                                     RowOff row_off, int j0, int khi, int g,
+                                                     int c16) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const float* kr = kp + row_off(min(j0 + 16 * st + c16, khi)) + 4 * g;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const float4 t = *reinterpret_cast<const float4*>(kr + 16 * c);
+                tl.kf[st][c][0] = t.x;
+                tl.kf[st][c][1] = t.y;
+                tl.kf[st][c][2] = t.z;
+                tl.kf[st][c][3] = t.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float* vr = vp + row_off(min(j0 + 16 * st + 4 * g + i, khi)) + NC * c16;
+#pragma unroll
+                for (int d4 = 0; d4 < NC; d4 += 4) {
+                    const float4 t = *reinterpret_cast<const float4*>(vr + d4);
+                    tl.vf[st][i][d4 + 0] = t.x;
+                    tl.vf[st][i][d4 + 1] = t.y;
+                    tl.vf[st][i][d4 + 2] = t.z;
+                    tl.vf[st][i][d4 + 3] = t.w;
+                }
+            }
+        }
+    }
+
+    // S^T = K Q^T: lane (g, c16) gets the scores of keys j0 + 16 st + 4g + i for row c16.
+    __device__ __forceinline__ void scores(const Tile& tl, floatx4 (&sacc)[2]) const {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            sacc[st] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    sacc[st] = mfma4(tl.kf[st][c][kk], q[c][kk], sacc[st]);
+        }
+    }
+
+    // O^T += V^T P^T (accumulator row c of block dt is output dim NC c + dt).
+    __device__ __forceinline__ static void pv(const Tile& tl, const float (&p)[2][4],
+                                              floatx4 (&oacc)[NC]) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int dt = 0; dt < NC; ++dt)
+                    oacc[dt] = mfma4(tl.vf[st][i][dt], p[st][i], oacc[dt]);
+    }
+};
+
+// f16 / bf16 K/V on v_mfma_f32_16x16x32_{f16,bf16}; Q and P as hi + lo terms.
+template <typename KV, int D>
+struct Operands {
+    static constexpr int NC = D / 16;
+    static constexpr int NK = D / 32;  // 32-dim chunks of a row = 32-bit words of NC dims
+    using T = uint16_t;
+    // Q^T operand terms: lane (g, c16) holds Q[row][32c + 8g + e], e = 0..7.
+    uint4 qh[NK], ql[NK];
+    struct Tile {
+        // K operand of block st: lane (g, c16) holds K[j0 + 16 st + c16][32c + 8g + e].
+        uint4 k[2][NK];
+        // Lane (g, c16): V[j0 + 16 st + 4g + i][NC c16 + 2w + (0, 1)] in word w.
+        uint32_t v[2][4][NK];
+    };
+
+    __device__ __forceinline__ void load_q(const float* row, float qs, int g) {
+#pragma unroll
+        for (int c = 0; c < NK; ++c) {
+            const float4 a = *reinterpret_cast<const float4*>(row + 32 * c + 8 * g);
+            const float4 b = *reinterpret_cast<const float4*>(row + 32 * c + 8 * g + 4);
+            split_pair(KV{}, a.x * qs, a.y * qs, qh[c].x, ql[c].x);
+            split_pair(KV{}, a.z * qs, a.w * qs, qh[c].y, ql[c].y);
+            split_pair(KV{}, b.x * qs, b.y * qs, qh[c].z, ql[c].z);
+            split_pair(KV{}, b.z * qs, b.w * qs, qh[c].w, ql[c].w);
+        }
+    }
+
+    template <class RowOff>
+    __device__ __forceinline__ static void load_tile(Tile& tl, const T* kp, const T* vp,
+                                                     RowOff row_off, int j0, int khi, int g,
+                                                     int c16) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const T* kr = kp + row_off(min(j0 + 16 * st + c16, khi)) + 8 * g;
+#pragma unroll
+            for (int c = 0; c < NK; ++c) tl.k[st][c] = *reinterpret_cast<const uint4*>(kr + 32 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const T* vr = vp + row_off(min(j0 + 16 * st + 4 * g + i, khi)) + NC * c16;
+                if constexpr (NK == 2) {
+                    const uint2 t = *reinterpret_cast<const uint2*>(vr);
+                    tl.v[st][i][0] = t.x;
+                    tl.v[st][i][1] = t.y;
+                } else {
+#pragma unroll
+                    for (int w = 0; w < NK; w += 4) {
+                        const uint4 t = *reinterpret_cast<const uint4*>(vr + 2 * w);
+                        tl.v[st][i][w + 0] = t.x;
+                        tl.v[st][i][w + 1] = t.y;
+                        tl.v[st][i][w + 2] = t.z;
+                        tl.v[st][i][w + 3] = t.w;
+                    }
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void scores(const Tile& tl, floatx4 (&sacc)[2]) const {
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            sacc[st] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NK; ++c) sacc[st] = mfma32(KV{}, tl.k[st][c], qh[c], sacc[st]);
+#pragma unroll
+            for (int c = 0; c < NK; ++c) sacc[st] = mfma32(KV{}, tl.k[st][c], ql[c], sacc[st]);
+        }
+    }
+
+    __device__ __forceinline__ static void pv(const Tile& tl, const float (&p)[2][4],
+                                              floatx4 (&oacc)[NC]) {
+        // P^T operand: element e = p[e / 4][e % 4], as hi and lo terms.
+        uint4 ph, pl;
+        split_pair(KV{}, p[0][0], p[0][1], ph.x, pl.x);
+        split_pair(KV{}, p[0][2], p[0][3], ph.y, pl.y);
+        split_pair(KV{}, p[1][0], p[1][1], ph.z, pl.z);
+        split_pair(KV{}, p[1][2], p[1][3], ph.w, pl.w);
+#pragma unroll
+        for (int dt = 0; dt < NC; ++dt) {
+            // V^T operand of dim block dt: element e = V[key e][NC c16 + dt].
+            const int w = dt >> 1, sel = dt & 1;
+            uint4 va;
+            va.x = pair_halves(tl.v[0][0][w], tl.v[0][1][w], sel);
+            va.y = pair_halves(tl.v[0][2][w], tl.v[0][3][w], sel);
+            va.z = pair_halves(tl.v[1][0][w], tl.v[1][1][w], sel);
+            va.w = pair_halves(tl.v[1][2][w], tl.v[1][3][w], sel);
+            oacc[dt] = mfma32(KV{}, va, ph, oacc[dt]);
+            oacc[dt] = mfma32(KV{}, va, pl, oacc[dt]);
+        }
+    }
 };
 
 template <typename KV, int D>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 4 : 2)))
     prefill_kernel(PrefillArgs a) {
     using T = typename KV::storage;
+    using Ops = Operands<KV, D>;
     constexpr int NC = D / 16;             // 16-wide dimension blocks
 
     __shared__ int s_tbl[kTablePages];
@@ -112,21 +307,9 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
 
     const int32_t* trow = a.page_table + (size_t)ti * a.max_pages;
 
-    // Q^T operand: lane (g, c16) holds Q[row][16c + 4g + kk], kk = 0..3.
-    float qr[NC][4];
-    {
-        const float* qp =
-            a.q + ((size_t)(start + min(r, len - 1)) * a.num_q_heads + h) * D + 4 * g;
-        const float qs = rvalid ? a.qscale : 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const float4 t = *reinterpret_cast<const float4*>(qp + 16 * c);
-            qr[c][0] = t.x * qs;
-            qr[c][1] = t.y * qs;
-            qr[c][2] = t.z * qs;
-            qr[c][3] = t.w * qs;
-        }
-    }
+    Ops ops;
+    ops.load_q(a.q + ((size_t)(start + min(r, len - 1)) * a.num_q_heads + h) * D,
+               rvalid ? a.qscale : 0.f, g);
 
     const T* kp = reinterpret_cast<const T*>(a.k_pages) + (size_t)kvh * D;
     const T* vp = reinterpret_cast<const T*>(a.v_pages) + (size_t)kvh * D;
@@ -143,45 +326,19 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
         return (((size_t)page << pshift) | (size_t)(key & pmask)) * slot_stride;
     };
 
-    // Keys past khi are clamped onto khi (a valid row, so no branch guards a load: the wait
-    // for the current tile then never covers the loads of the next one).  Only the last
-    // slice has such keys (khi = kmax there); their scores are masked for every row, and
-    // their V rows are zeroed in compute_tile.
-    auto load_tile = [&](PrefillTile<D>& tl, int t) {
-        const int j0 = t * kTileKeys;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const T* kr = kp + row_off(min(j0 + 16 * st + c16, khi)) + 4 * g;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) load4<KV>(kr + 16 * c, tl.kf[st][c]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const T* vr = vp + row_off(min(j0 + 16 * st + 4 * g + i, khi)) + NC * c16;
-#pragma unroll
-                for (int d4 = 0; d4 < NC; d4 += 4) load4<KV>(vr + d4, &tl.vf[st][i][d4]);
-            }
-        }
-    };
-
     float m = -INFINITY;
     float lsum = 0.f;
     floatx4 oacc[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) oacc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute_tile = [&](const PrefillTile<D>& tl, int t) {
+    // Keys past khi are clamped onto khi (a valid row, so no branch guards a load: the wait
+    // for the current tile then never covers the loads of the next one).  Only the last
+    // slice has such keys (khi = kmax there); their scores are masked for every row.
+    auto compute_tile = [&](const typename Ops::Tile& tl, int t) {
         const int j0 = t * kTileKeys;
-        // S^T = K Q^T: lane (g, c16) gets scores of keys j0 + 16 st + 4g + i for row c16.
         floatx4 sacc[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            sacc[st] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    sacc[st] = mfma16(tl.kf[st][c][kk], qr[c][kk], sacc[st]);
-        }
+        ops.scores(tl, sacc);
 
         float tmax = -INFINITY;
         float s[2][4];
@@ -210,19 +367,7 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
         m = mn;
 #pragma unroll
         for (int dt = 0; dt < NC; ++dt) oacc[dt] *= alpha;
-
-        // O^T += V^T P^T (accumulator row c of block dt is output dim NC c + dt).  A key past
-        // khi holds a copy of row khi: its V is zeroed so that its zero weight leaves O
-        // unchanged whatever that row holds.
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool vok = j0 + 16 * st + 4 * g + i <= khi;
-#pragma unroll
-                for (int dt = 0; dt < NC; ++dt)
-                    oacc[dt] = mfma16(vok ? tl.vf[st][i][dt] : 0.f, p[st][i], oacc[dt]);
-            }
+        Ops::pv(tl, p, oacc);
     };
 
     // This wave's tiles of a slice: t = t0 + w, t0 + w + 8, ... with w = (wave + block) % 8,
@@ -232,8 +377,8 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     const int first = (wave + (r0 / kRows)) % kWaves;
     auto run_tiles = [&](int t, int t_end) {
         for (; t < t_end; t += kWaves) {
-            PrefillTile<D> tl;
-            load_tile(tl, t);
+            typename Ops::Tile tl;
+            Ops::load_tile(tl, kp, vp, row_off, t * kTileKeys, khi, g, c16);
             compute_tile(tl, t);
         }
     };
@@ -291,16 +436,14 @@ hipError_t launch_typed(const PrefillArgs& a, int q_blocks, hipStream_t stream) 
 
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int q_blocks,
                           hipStream_t stream) {
-    (void)q_blocks;
-    const int qb = q_blocks;
     if (head_dim == 64) {
-        if (kv_dtype == 0) return launch_typed<F32, 64>(a, qb, stream);
-        if (kv_dtype == 1) return launch_typed<F16, 64>(a, qb, stream);
-        return launch_typed<BF16, 64>(a, qb, stream);
+        if (kv_dtype == 0) return launch_typed<F32, 64>(a, q_blocks, stream);
+        if (kv_dtype == 1) return launch_typed<F16, 64>(a, q_blocks, stream);
+        return launch_typed<BF16, 64>(a, q_blocks, stream);
     }
-    if (kv_dtype == 0) return launch_typed<F32, 128>(a, qb, stream);
-    if (kv_dtype == 1) return launch_typed<F16, 128>(a, qb, stream);
-    return launch_typed<BF16, 128>(a, qb, stream);
+    if (kv_dtype == 0) return launch_typed<F32, 128>(a, q_blocks, stream);
+    if (kv_dtype == 1) return launch_typed<F16, 128>(a, q_blocks, stream);
+    return launch_typed<BF16, 128>(a, q_blocks, stream);
 }
 
 }  // namespace pa

@@ -79,7 +79,7 @@ def rng_for(case_id) -> np.random.Generator:
 
 
 def named_rng(index: int) -> np.random.Generator:
-    ss = np.random.SeedSequence(MASTER_SEED).spawn(7)[index]   # child i does not depend on n
+    ss = np.random.SeedSequence(MASTER_SEED).spawn(8)[index]   # child i does not depend on n
     return np.random.Generator(np.random.PCG64(ss))
 
 
@@ -151,6 +151,12 @@ WORKLOADS = {
         name="decode_hq16_hkv8_d256_ctx4096_bf16", kind="decode", index=6, hq=16, hkv=8,
         head_dim=256, page_size=16, dtype="bf16", ctx=(4096,), num_pages=256, num_splits=32,
         layers=16, description="head_dim-256 decode, batch 1, 16 layers per step"),
+    # The 512-token prefill in crucible's production GQA geometry (12 query heads over 3 kv
+    # heads) with a bf16 pool: the measurement shape of the 16-bit MFMA prefill.
+    "prefill_hq12_hkv3_d64_t512_bf16": Workload(
+        name="prefill_hq12_hkv3_d64_t512_bf16", kind="prefill", index=7, hq=12, hkv=3,
+        head_dim=64, page_size=16, dtype="bf16", tokens=512, num_pages=32, scale=0.125,
+        description="causal packed prefill of one 512-token sequence, GQA 12/3, bf16 pool"),
 }
 
 

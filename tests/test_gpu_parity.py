@@ -278,6 +278,23 @@ def test_prefill_workload():
     assert_within(got, ref, 1e-5, 0.0, "prefill 512")
 
 
+def test_prefill_workload_bf16():
+    """The 16-bit MFMA prefill at its measurement shape.  Besides the bf16 bar, the error
+    stays near f32 rounding (2^-16 |x| split residual of Q and P): a kernel that rounded Q or
+    P to bf16 once would err by ~1e-3 here."""
+    w = wl.WORKLOADS["prefill_hq12_hkv3_d64_t512_bf16"]
+    case = wl.workload_prefill_case(w)
+    announce("prefill workload 512 tokens 12/3 d64 bf16")
+    got, gk, gv = run_prefill(case)
+    ref, kp, vp, count = oracle_prefill(case)
+    assert count == 131328
+    assert_bitwise(gk, kp, "K pool after write")
+    assert_within(got, ref, *tolerance("bf16"), "prefill 512 bf16")
+    err = float(np.max(np.abs(got.astype(np.float64) - ref)))
+    print(f"prefill 512 bf16: max abs error {err:.3e}")
+    assert err < 1e-4, err
+
+
 PREFILL_CASES = [
     # hq, hkv, d, ps, dtype, starts, lens, gap
     (12, 3, 64, 16, "f32", [0, 63, 255, 512], [17, 64, 129, 257], 0),   # heterogeneous
@@ -287,6 +304,11 @@ PREFILL_CASES = [
     (40, 8, 128, 16, "f16", [3000], [70], 0),
     (4, 4, 64, 1, "f32", [5, 0], [20, 33], 2),
     (16, 1, 128, 16, "bf16", [0], [129], 0),
+    (12, 3, 64, 16, "bf16", [0, 63, 255, 512], [17, 64, 129, 257], 0),  # heterogeneous
+    (12, 3, 64, 16, "f16", [64] * 4, [64] * 4, 0),                      # history-64-at-64
+    (8, 8, 64, 1, "f16", [5, 0], [20, 33], 2),
+    (12, 4, 128, 32, "f16", [0, 2000], [200, 40], 3),
+    (8, 2, 128, 16, "bf16", [16400, 0], [64, 31], 0),   # key range past one page-id slice
 ]
 
 
