@@ -7,7 +7,8 @@
   (crucible README, gpu-batch check);
 * GQA equals MHA with K/V repeated per group (crucible README, "Tests");
 * repeated runs are bit-identical; poisoned never-read bytes never reach an output;
-* a prefill segment's rows do not depend on the other segments packed with it."""
+* a prefill segment's rows do not depend on the other segments packed with it;
+* sequences of context 0 in a batch give zero rows and leave the other rows unchanged."""
 import numpy as np
 import pytest
 import torch
@@ -95,7 +96,7 @@ def test_batch_composition_bitwise():
     assert_bitwise(_decode(rev)[0][order], full, "reversed batch order")
 
 
-@pytest.mark.parametrize("g", [4, 5, 7, 8, 12])
+@pytest.mark.parametrize("g", [4, 5, 7, 8, 12, 33, 64])
 def test_gqa_equals_repeated_kv_mha_bitwise(g):
     announce(f"GQA g={g} vs MHA bitwise")
     rng = wl.rng_for([603, g])
@@ -156,3 +157,35 @@ def test_prefill_segment_isolation_bitwise():
             v_new=case.v_new[rows], token_table_index=case.token_table_index[rows],
             token_position=case.token_position[rows], dtype=case.dtype, scale=case.scale)
         assert_bitwise(run(alone), full[rows], f"segment {i} alone vs packed")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,S", [("f16", 40, 8, 128, 32), ("f32", 12, 3, 64, 7)])
+def test_empty_sequences_in_a_batch(dtype, hq, hkv, d, S):
+    """Sequences of context 0 (free slots of a continuous batch) give zero rows and idle
+    partials; the other rows are those of the same batch without them, bit for bit; the
+    single-launch step agrees with the three-launch step and leaves its counters at zero."""
+    announce(f"empty sequences in a batch {dtype} {hq}/{hkv} d={d} S={S}")
+    rng = wl.rng_for([606, hq, d])
+    ctx = [0, 300, 0, 5]
+    case = wl.make_decode_case(rng, batch=4, hq=hq, hkv=hkv, head_dim=d, page_size=16,
+                               dtype=dtype, ctx=ctx, num_splits=S)
+    run = DecodeRun(case)
+    out = run.step()
+    po, pml = host(run.po), host(run.pml)
+    empty = [0, 2]
+    assert np.all(out[empty] == 0.0), "an empty sequence's output must be zero"
+    assert np.all(pml[empty][..., 0] == -np.inf) and np.all(pml[empty][..., 1] == 0.0)
+    assert np.all(po[empty] == 0.0)
+    live = [1, 3]
+    sub = wl.DecodeCase(
+        q=case.q[live], k_pages=case.k_pages, v_pages=case.v_pages,
+        page_table=case.page_table[live], context_lens=case.context_lens[live],
+        k_new=case.k_new[live], v_new=case.v_new[live],
+        token_table_index=np.arange(2, dtype=np.int32), token_position=case.token_position[live],
+        dtype=case.dtype, scale=case.scale, num_splits=case.num_splits)
+    assert_bitwise(out[live], DecodeRun(sub).step(), "live rows vs the batch without empties")
+    fused = DecodeRun(case)
+    got = fused.fused_step()
+    assert_bitwise(got, out, "single-launch step vs three launches")
+    assert int(fused.counters.abs().sum().item()) == 0, "counters must be left at zero"
+    assert_bitwise(host(fused.kp), host(run.kp), "pool after the single-launch write")

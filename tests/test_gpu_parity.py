@@ -122,7 +122,10 @@ BOUNDARY_CTX = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 25
 @pytest.mark.parametrize("geom", [(40, 8, 128, 16, "f16", 32), (28, 4, 128, 16, "f16", 32),
                                   (64, 8, 128, 32, "bf16", 16), (8, 2, 64, 16, "f32", 16),
                                   (12, 3, 64, 16, "f32", 8), (16, 16, 128, 32, "bf16", 4),
-                                  (32, 2, 64, 16, "bf16", 8), (12, 1, 128, 16, "f16", 16)],
+                                  (32, 2, 64, 16, "bf16", 8), (12, 1, 128, 16, "f16", 16),
+                                  # the largest group (8 head groups of 8) and a ragged one
+                                  # (groups of 7, the last with 5 heads)
+                                  (64, 1, 128, 16, "bf16", 8), (33, 1, 64, 16, "f16", 16)],
                          ids=lambda g: "hq{}_hkv{}_d{}_ps{}_{}_S{}".format(*g))
 def test_decode_boundary_lengths(geom):
     """Every boundary length of the pages' fixture lists in one batch."""
@@ -206,7 +209,8 @@ def test_decode_fused_split_counts(splits):
 
 
 @pytest.mark.parametrize("geom", [(40, 8, 128, 16, "f16", 32), (8, 2, 64, 16, "f32", 16),
-                                  (24, 2, 128, 32, "bf16", 8), (4, 4, 64, 1, "bf16", 5)],
+                                  (24, 2, 128, 32, "bf16", 8), (4, 4, 64, 1, "bf16", 5),
+                                  (64, 1, 128, 16, "bf16", 8), (33, 3, 128, 16, "f16", 8)],
                          ids=lambda g: "hq{}_hkv{}_d{}_ps{}_{}_S{}".format(*g))
 def test_decode_fused_boundary_lengths(geom):
     hq, hkv, d, ps, dtype, S = geom
