@@ -28,7 +28,7 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library allocates
- *     nothing, keeps no state between calls and is re-entrant (paged_attn_decode_fused keeps
+ *     nothing, keeps no data between calls and is re-entrant (paged_attn_decode_fused keeps
  *     its per-call state in the caller's counter buffer; see there).
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null stream).
  *     No call synchronises; ordering is stream order, so a kv_page_write enqueued before an

@@ -1,5 +1,6 @@
 // api.hip — the C ABI of include/paged_attn.h: host-side validation, then one launch per
-// kernel on the caller's stream.  No allocation, no synchronisation, no state.
+// kernel on the caller's stream.  No allocation and no synchronisation; the only state is
+// read-once device facts (a device's CU count, a kernel's raised dynamic-LDS limit).
 //
 // Every host scalar is checked before anything is enqueued (crucible, "Paged attention
 // results": malformed shapes, overflow and bad indices are rejected before device access).
@@ -8,6 +9,9 @@
 // arguments describe (clamped page ids, clamped lengths, skipped rows).
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
+#include <atomic>
 
 #include "../../include/paged_attn.h"
 #include "common.h"
@@ -23,6 +27,20 @@ constexpr int kMaxHeadsPerWg = 8;
 // Query heads one decode workgroup serves: 8, or 4 at head_dim 256 (q and the accumulators
 // of a lane are heads x D/16 floats each).
 int max_heads_per_wg(int head_dim) { return head_dim > 128 ? 4 : kMaxHeadsPerWg; }
+
+// Compute units of the current device, read once per device (0 if the runtime cannot say).
+int compute_units() {
+    static std::atomic<int> cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -105,7 +123,20 @@ int make_decode_args(const float* q, const void* k_pages, const void* v_pages, i
         return PA_EINVAL;
     const int group = num_q_heads / num_kv_heads;
     const int max_heads = max_heads_per_wg(head_dim);
-    const int head_groups = (group + max_heads - 1) / max_heads;
+    int head_groups = (group + max_heads - 1) / max_heads;
+    // A grid with fewer workgroups than the device has CUs leaves CUs idle: then the query
+    // heads of a KV head are spread over twice the workgroups.  Each reads that KV head's
+    // rows; workgroups are dealt to the 8 XCDs in turn, so with a split count that is a
+    // multiple of 8 the two workgroups of a split share an XCD and the second read mostly hits
+    // its L2.  Every head grouping sums in the same order, so the result is the same to the
+    // bit.  Twice ceil(group / 8) groups is what the single-launch step's counter buffer
+    // holds per KV head.  Workgroups of fewer than 3 heads cost more in duplicated row reads
+    // than they gain (measured: 8/2 heads at context 256 went 8.0 -> 8.4 us with groups of 2;
+    // 28/4 heads at context 1641 went 12.5 -> 12.0 us with groups of 4 and 3).
+    const int cap_groups = 2 * ((group + kMaxHeadsPerWg - 1) / kMaxHeadsPerWg);
+    if ((int64_t)num_seqs * num_kv_heads * head_groups * num_splits < compute_units() &&
+        2 * head_groups <= cap_groups && (group + 2 * head_groups - 1) / (2 * head_groups) >= 3)
+        head_groups *= 2;
     const int heads_per_wg = (group + head_groups - 1) / head_groups;
     if ((int64_t)num_kv_heads * head_groups > kMaxGridYZ) return PA_EUNSUPPORTED;
 
