@@ -40,24 +40,6 @@ __device__ __forceinline__ void widen_word(BF16, uint32_t w, float* out) {
     out[1] = __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
-// Widen one 16-byte vector (4 words) into 16 / kBytes floats.
-template <typename KV>
-__device__ __forceinline__ void widen16(const uint4& v, float* out) {
-    constexpr int per = 4 / KV::kBytes;
-    widen_word(KV{}, v.x, out + 0 * per);
-    widen_word(KV{}, v.y, out + 1 * per);
-    widen_word(KV{}, v.z, out + 2 * per);
-    widen_word(KV{}, v.w, out + 3 * per);
-}
-
-// Widen one element given its raw bits (low kBytes bytes of `bits`).
-template <typename KV>
-__device__ __forceinline__ float widen1(uint32_t bits) {
-    float f[2];
-    widen_word(KV{}, bits, f);
-    return f[0];
-}
-
 // ---------------------------------------------------------------- cross-lane reductions
 
 // DPP move within 16-lane rows (the source lane always exists for these controls).
@@ -67,10 +49,6 @@ __device__ __forceinline__ float dpp_mov(float v) {
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
 }
 
-constexpr int kDppQuadXor1 = 0xb1;     // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4e;     // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <- lane 7-i within 8
-constexpr int kDppMirror = 0x140;      // row_mirror: lane i <- lane 15-i within 16
 constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i <- lane (i+8) mod 16 (= xor 8)
 
 // Exchanges across 16-lane rows go through the LDS crossbar: ds_swizzle for xor 16 (inside
@@ -84,32 +62,8 @@ __device__ __forceinline__ float lane_xor16(float v) {
 }
 __device__ __forceinline__ float lane_xor32(float v) { return __shfl_xor(v, 32); }
 
-// All-reduce over aligned groups of N lanes (N a power of two, 1..64).  Every lane of a
-// group ends with the bit-identical result: each step combines the same two operands.
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-    if constexpr (N >= 2) v += dpp_mov<kDppQuadXor1>(v);
-    if constexpr (N >= 4) v += dpp_mov<kDppQuadXor2>(v);
-    if constexpr (N >= 8) v += dpp_mov<kDppHalfMirror>(v);
-    if constexpr (N >= 16) v += dpp_mov<kDppMirror>(v);
-    if constexpr (N >= 32) v += lane_xor16(v);
-    if constexpr (N >= 64) v += lane_xor32(v);
-    return v;
-}
-
-template <int N>
-__device__ __forceinline__ float group_max(float v) {
-    if constexpr (N >= 2) v = fmaxf(v, dpp_mov<kDppQuadXor1>(v));
-    if constexpr (N >= 4) v = fmaxf(v, dpp_mov<kDppQuadXor2>(v));
-    if constexpr (N >= 8) v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
-    if constexpr (N >= 16) v = fmaxf(v, dpp_mov<kDppMirror>(v));
-    if constexpr (N >= 32) v = fmaxf(v, lane_xor16(v));
-    if constexpr (N >= 64) v = fmaxf(v, lane_xor32(v));
-    return v;
-}
-
-// Reduction ACROSS the groups of N lanes of a wave (lanes with the same index within their
-// group combine): the complement of group_sum / group_max.
+// Reduction ACROSS the groups of N lanes of a wave: lanes with the same index within their
+// group of N combine, and every lane ends with the same result for its index.
 template <int N>
 __device__ __forceinline__ float across_groups_sum(float v) {
     if constexpr (N <= 8) v += dpp_mov<kDppRor8>(v);
