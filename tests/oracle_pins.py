@@ -147,6 +147,21 @@ def pin_two_key_sigmoid(orc):
     assert abs(out[0, 0, 0] - expect) < 1e-15, (out[0, 0, 0], expect)
 
 
+def pin_worked_example_three_quarters(orc):
+    """The worked two-key example: D=1, scale 1, q=1, keys [0, ln 3], values [0, 1].  The
+    weights are [1/4, 3/4], so the output is 3/4 (to the rounding of ln 3 to f32, whose
+    exact effect is checked too)."""
+    k1 = np.float32(math.log(3.0))
+    kp = np.array([0.0, k1], np.float32).reshape(1, 2, 1, 1)
+    vp = np.array([0.0, 1.0], np.float32).reshape(1, 2, 1, 1)
+    q = np.ones((1, 1, 1), np.float32)
+    out = orc.decode(q, kp, vp, "f32", np.zeros((1, 1), np.int32), np.array([2], np.int32),
+                     1.0)
+    e = math.exp(float(k1))
+    assert abs(out[0, 0, 0] - e / (1.0 + e)) < 1e-15, out[0, 0, 0]
+    assert abs(out[0, 0, 0] - 0.75) < 1e-7, out[0, 0, 0]
+
+
 def pin_ctx1_returns_v0(orc):
     rng = wl.rng_for(101)
     for dtype in ("f32", "f16", "bf16"):
@@ -694,7 +709,8 @@ def _golden_causal():
 
 
 PINS = [
-    pin_f16_exhaustive, pin_bf16_exhaustive, pin_two_key_sigmoid, pin_ctx1_returns_v0,
+    pin_f16_exhaustive, pin_bf16_exhaustive, pin_two_key_sigmoid,
+    pin_worked_example_three_quarters, pin_ctx1_returns_v0,
     pin_zero_query_mean, pin_decode_vs_sdpa, pin_outlier_data_vs_sdpa, pin_page_permutation,
     pin_gqa_equals_mha, pin_batch_invariance, pin_future_poison, pin_split_rule_golden,
     pin_split_partition, pin_split_combine_equals_unsplit, pin_idle_splits,
