@@ -42,6 +42,13 @@
  *     arguments describe: out-of-range page ids are clamped (attention) or the row is
  *     skipped (write), and lengths are clamped to max_pages_per_seq * page_size; the
  *     numerical result for such input is unspecified.
+ *   - Checked build (libpaged_attn_checked.so, compiled with -DPAGED_ATTN_CHECKED): the same
+ *     entry points, whose kernels also record the device metadata they clamp or skip --
+ *     a length outside [0, capacity], a page id outside [0, num_pages) among the positions
+ *     a call reads or writes, a malformed prefill descriptor, a write to a missing table row
+ *     or beyond the table's capacity (a negative owner or position remains an explicit
+ *     skip).  Each call then synchronises its stream and returns PA_EDATA if anything was
+ *     recorded.  It is a debugging aid: it synchronises, so it is not for graph capture.
  *   - Layouts are dense row-major with the innermost dimension last:
  *       q            [tokens][Hq][D]                    f32
  *       K/V pages    [num_pages][page_size][Hkv][D]     kv_dtype
@@ -68,7 +75,8 @@ typedef enum pa_status {
     PA_OK = 0,
     PA_EINVAL = -1,        /* malformed argument: null pointer, bad shape, overflow          */
     PA_EUNSUPPORTED = -2,  /* well-formed but not built: head_dim, dtype, group size          */
-    PA_ELAUNCH = -3        /* the HIP runtime rejected a launch (no device, bad stream, ...)  */
+    PA_ELAUNCH = -3,       /* the HIP runtime rejected a launch (no device, bad stream, ...)  */
+    PA_EDATA = -4          /* checked build only: device metadata out of range (see below)    */
 } pa_status;
 
 /* Short English text for a status code (static storage, never NULL). */

@@ -15,8 +15,12 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
+# The checked build: the same entry points, which also report out-of-range device metadata
+# (PA_EDATA) after synchronising.  Selected with use_checked_library() or, at import,
+# PAGED_ATTN_CHECKED=1 in the environment.
+CHECKED_LIB_PATH = os.path.join(_HERE, "libpaged_attn_checked.so")
 
-PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_ELAUNCH = 0, -1, -2, -3
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_ELAUNCH, PA_EDATA = 0, -1, -2, -3, -4
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_ROPE_ADJACENT, PA_ROPE_HALVES = 0, 1
 
@@ -32,18 +36,26 @@ class PagedAttnError(RuntimeError):
         super().__init__(f"{fn} failed: {status} ({paged_attn_status_string(status)})")
 
 
-_lib = None
+_libs = {}
+_checked = os.environ.get("PAGED_ATTN_CHECKED", "") == "1"
 
 
-def raw_library():
-    """The loaded ``ctypes.CDLL`` with argument types set (pointers as ``c_void_p``)."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
+def use_checked_library(flag: bool = True) -> None:
+    """Route the functions of this module to the checked build (flag=True) or back."""
+    global _checked
+    _checked = bool(flag)
+
+
+def raw_library(checked: bool | None = None):
+    """The loaded ``ctypes.CDLL`` with argument types set (pointers as ``c_void_p``): the
+    product library, or the checked build when selected."""
+    path = CHECKED_LIB_PATH if (_checked if checked is None else checked) else LIB_PATH
+    if path not in _libs:
+        if not os.path.exists(path):
             raise ImportError(
-                f"{LIB_PATH} is missing: build it with "
+                f"{path} is missing: build it with "
                 "`python -m paged_gqa_attention_decode_amd.build` (there is no fallback)")
-        lib = ctypes.CDLL(LIB_PATH)
+        lib = ctypes.CDLL(path)
         p, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.paged_attn_status_string.argtypes = [i]
         lib.paged_attn_status_string.restype = ctypes.c_char_p
@@ -64,8 +76,8 @@ def raw_library():
         for name in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_combine",
                      "paged_attn_prefill", "kv_page_write", "kv_page_write_rope"):
             getattr(lib, name).restype = ctypes.c_int
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return _libs[path]
 
 
 def paged_attn_status_string(status: int) -> str:

@@ -1,9 +1,11 @@
-"""Build libpaged_attn.so from csrc/*.hip with hipcc for gfx950.
+"""Build libpaged_attn.so, and its checked variant libpaged_attn_checked.so, from csrc/*.hip
+with hipcc for gfx950.
 
     python -m paged_gqa_attention_decode_amd.build
 
-Each translation unit compiles separately (in parallel) to an object under _build/, then
-hipcc links the shared library next to this file.  Packed-FP32 instructions are disabled
+Each translation unit compiles separately (in parallel) to an object under _build/ (the
+checked variant, with -DPAGED_ATTN_CHECKED, under _build_checked/), then hipcc links the
+shared library next to this file.  Packed-FP32 instructions are disabled
 (-target-feature -packed-fp32-ops); all arithmetic is ordinary f32.
 """
 from __future__ import annotations
@@ -17,6 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpaged_attn.so")
+BUILD_CHECKED = os.path.join(HERE, "_build_checked")
+LIB_CHECKED = os.path.join(HERE, "libpaged_attn_checked.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["api.hip", "decode.hip", "combine.hip", "prefill.hip", "kv_write.hip",
@@ -25,8 +29,8 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str, extra=()) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra=(), build_dir=None) -> str:
+    obj = os.path.join(build_dir or BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC] + FLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -34,23 +38,31 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source and link libpaged_attn.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), checked: bool = False) -> str:
+    """Compile every source and link libpaged_attn.so (or, with checked=True,
+    libpaged_attn_checked.so); returns its path."""
+    build_dir, lib = (BUILD_CHECKED, LIB_CHECKED) if checked else (BUILD, LIB)
+    flags = tuple(extra_flags) + (("-DPAGED_ATTN_CHECKED",) if checked else ())
+    os.makedirs(build_dir, exist_ok=True)
     jobs = min(len(SOURCES), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, flags, build_dir), SOURCES))
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def build_all(verbose: bool = False):
+    """Both libraries: the product and its checked variant."""
+    return build(verbose), build(verbose, checked=True)
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build_all(verbose=True)
     sys.exit(0)

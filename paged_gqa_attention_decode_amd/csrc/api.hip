@@ -71,7 +71,25 @@ int check_pages(int kv_dtype, int num_q_heads, int num_kv_heads, int head_dim, i
     return PA_OK;
 }
 
-int launched(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ELAUNCH; }
+// Status of an enqueued call.  The checked build then waits for the stream and reports
+// device metadata that a kernel found out of range (and clamped or skipped) as PA_EDATA.
+int launched(hipError_t e, void* stream) {
+    if (e != hipSuccess) return PA_ELAUNCH;
+    if constexpr (!pa::kChecked) {
+        (void)stream;
+        return PA_OK;
+    } else {
+        if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return PA_ELAUNCH;
+        int any = 0;
+        for (auto take : {pa::take_bad_metadata_decode, pa::take_bad_metadata_prefill,
+                          pa::take_bad_metadata_kv_write, pa::take_bad_metadata_kv_write_rope}) {
+            int bad = 0;
+            if (take(&bad) != hipSuccess) return PA_ELAUNCH;
+            any |= bad;
+        }
+        return any ? PA_EDATA : PA_OK;
+    }
+}
 
 }  // namespace
 
@@ -83,6 +101,7 @@ const char* paged_attn_status_string(int status) {
         case PA_EINVAL: return "invalid argument";
         case PA_EUNSUPPORTED: return "unsupported configuration";
         case PA_ELAUNCH: return "kernel launch failed";
+        case PA_EDATA: return "device metadata out of range (checked build)";
         default: return "unknown status";
     }
 }
@@ -181,7 +200,8 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
                               num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                               max_pages_per_seq, scale, window, num_splits, partial_o, partial_ml, &a);
     if (rc != PA_OK) return rc;
-    return launched(pa::launch_decode(a, kv_dtype, head_dim, false, (hipStream_t)stream));
+    return launched(pa::launch_decode(a, kv_dtype, head_dim, false, (hipStream_t)stream),
+                    stream);
 }
 
 size_t paged_attn_decode_fused_counters(int num_seqs, int num_q_heads, int num_kv_heads) {
@@ -214,7 +234,8 @@ int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new
     a.v_pages_w = v_pages;
     a.counters = counters;
     a.out = out;
-    return launched(pa::launch_decode(a, kv_dtype, head_dim, true, (hipStream_t)stream));
+    return launched(pa::launch_decode(a, kv_dtype, head_dim, true, (hipStream_t)stream),
+                    stream);
 }
 
 int paged_attn_combine(const float* partial_o, const float* partial_ml, int num_seqs,
@@ -232,7 +253,7 @@ int paged_attn_combine(const float* partial_o, const float* partial_ml, int num_
     a.out = out;
     a.rows = num_seqs * num_q_heads;
     a.num_splits = num_splits;
-    return launched(pa::launch_combine(a, head_dim, (hipStream_t)stream));
+    return launched(pa::launch_combine(a, head_dim, (hipStream_t)stream), stream);
 }
 
 int paged_attn_prefill(const float* q, const void* k_pages, const void* v_pages,
@@ -275,7 +296,7 @@ int paged_attn_prefill(const float* q, const void* k_pages, const void* v_pages,
     if ((int64_t)q_blocks * num_q_heads > kI32Max) return PA_EUNSUPPORTED;
     a.q_blocks = q_blocks;
     return launched(
-        pa::launch_prefill(a, kv_dtype, head_dim, q_blocks, (hipStream_t)stream));
+        pa::launch_prefill(a, kv_dtype, head_dim, q_blocks, (hipStream_t)stream), stream);
 }
 
 int kv_page_write(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
@@ -311,7 +332,7 @@ int kv_page_write(const void* k_new, const void* v_new, void* k_pages, void* v_p
     a.page_shift = ilog2(page_size);
     a.num_pages = num_pages;
     a.max_pages = max_pages_per_seq;
-    return launched(pa::launch_kv_write(a, (hipStream_t)stream));
+    return launched(pa::launch_kv_write(a, (hipStream_t)stream), stream);
 }
 
 int kv_page_write_rope(const float* k_new, const float* v_new, void* k_pages, void* v_pages,
@@ -353,7 +374,7 @@ int kv_page_write_rope(const float* k_new, const float* v_new, void* k_pages, vo
     a.page_shift = ilog2(page_size);
     a.num_pages = num_pages;
     a.max_pages = max_pages_per_seq;
-    return launched(pa::launch_kv_write_rope(a, kv_dtype, (hipStream_t)stream));
+    return launched(pa::launch_kv_write_rope(a, kv_dtype, (hipStream_t)stream), stream);
 }
 
 }  // extern "C"

@@ -12,6 +12,22 @@ namespace pa {
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e): scores are kept in base-2 units
 constexpr float kLn2 = 0.6931471805599453f;    // ln(2): back to natural-log units on store
 
+// ---------------------------------------------------------------- checked build
+
+// Built with -DPAGED_ATTN_CHECKED, the kernels also record device metadata outside its
+// documented range -- under the same conditions in which every build clamps or skips it --
+// in a flag of their translation unit, which the entry points read after synchronising.
+#ifdef PAGED_ATTN_CHECKED
+constexpr bool kChecked = true;
+#else
+constexpr bool kChecked = false;
+#endif
+
+// Mark `flag` (a per-translation-unit device word) in the checked build; nothing otherwise.
+__device__ __forceinline__ void mark_bad(int* flag) {
+    if constexpr (kChecked) *reinterpret_cast<volatile int*>(flag) = 1;
+}
+
 // ---------------------------------------------------------------- cache element types
 
 struct F32 {
@@ -256,5 +272,25 @@ hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int 
                           hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 hipError_t launch_kv_write_rope(const KvRopeArgs& a, int kv_dtype, hipStream_t stream);
+
+// Checked build: read and clear each kernel file's metadata flag (synchronous copies; call
+// after the stream has been synchronised).  *bad is set when the flag was marked.
+hipError_t take_bad_metadata_decode(int* bad);
+hipError_t take_bad_metadata_prefill(int* bad);
+hipError_t take_bad_metadata_kv_write(int* bad);
+hipError_t take_bad_metadata_kv_write_rope(int* bad);
+
+// The body of the four functions above, over one file's flag.
+#define PA_DEFINE_TAKE_BAD_METADATA(NAME, FLAG)                                   \
+    hipError_t NAME(int* bad) {                                                   \
+        int v = 0;                                                                \
+        hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(FLAG), sizeof(int));    \
+        if (e == hipSuccess && v != 0) {                                          \
+            const int zero = 0;                                                   \
+            e = hipMemcpyToSymbol(HIP_SYMBOL(FLAG), &zero, sizeof(int));          \
+        }                                                                         \
+        *bad = v;                                                                 \
+        return e;                                                                 \
+    }
 
 }  // namespace pa

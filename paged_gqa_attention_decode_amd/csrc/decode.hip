@@ -36,6 +36,10 @@
 #include "common.h"
 
 namespace pa {
+
+// Checked build: set when a length or an attended page id is outside its range.
+__device__ int g_bad_metadata_decode;
+
 namespace {
 
 // f(std::integral_constant<int, I>) for I in [I0, I1): a loop whose index is a constant.
@@ -304,6 +308,20 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     }
     const int cap = a.max_pages << a.page_shift;
     const int ctx = clampi(a.context_lens[b], 0, cap);
+    if constexpr (kChecked) {
+        // The length within [0, capacity], and (one workgroup per sequence and KV head) the
+        // page ids of the attended positions within [0, num_pages).
+        const int raw = a.context_lens[b];
+        if (raw < 0 || raw > cap) mark_bad(&g_bad_metadata_decode);
+        if (split == 0 && hg == 0) {
+            const int first = (a.window > 0 && ctx > a.window) ? ctx - a.window : 0;
+            const int p_end = (ctx + (1 << a.page_shift) - 1) >> a.page_shift;
+            for (int p = (first >> a.page_shift) + tid; p < p_end; p += nthreads) {
+                const int v = trow[p];
+                if (v < 0 || v >= a.num_pages) mark_bad(&g_bad_metadata_decode);
+            }
+        }
+    }
     // q in the lane's register order: register B + r of group (N, B) holds head
     // B + (r ^ slot_key<N>(li)); padded heads repeat the last real one.
     float qv[GH][EPL];
@@ -777,6 +795,8 @@ hipError_t launch_all(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream
 }
 
 }  // namespace
+
+PA_DEFINE_TAKE_BAD_METADATA(take_bad_metadata_decode, g_bad_metadata_decode)
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, bool fused,
                          hipStream_t stream) {

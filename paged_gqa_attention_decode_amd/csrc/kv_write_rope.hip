@@ -24,6 +24,11 @@
 #include "common.h"
 
 namespace pa {
+
+// Checked build: as for kv_page_write, a token to be written whose table row, position or
+// page id is out of range (negative owner or position: an explicit skip).
+__device__ int g_bad_metadata_kv_write_rope;
+
 namespace {
 
 // Two f32 values rounded to the pool dtype and packed into one 32-bit word.
@@ -131,10 +136,16 @@ __global__ void __launch_bounds__(256) kv_write_rope_kernel(KvRopeArgs a) {
     }
 
     const int owner = a.token_table_index[tok];
-    if (owner < 0 || owner >= a.num_tables) return;
-    if (pos >= (a.max_pages << a.page_shift)) return;
+    if (owner < 0) return;
+    if (owner >= a.num_tables || pos >= (a.max_pages << a.page_shift)) {
+        if (u == 0) mark_bad(&g_bad_metadata_kv_write_rope);
+        return;
+    }
     const int page = a.page_table[(size_t)owner * a.max_pages + (pos >> a.page_shift)];
-    if (page < 0 || page >= a.num_pages) return;
+    if (page < 0 || page >= a.num_pages) {
+        if (u == 0) mark_bad(&g_bad_metadata_kv_write_rope);
+        return;
+    }
     const size_t slot = ((size_t)page << a.page_shift) | (size_t)(pos & ((1 << a.page_shift) - 1));
     const size_t dst = (slot * a.num_kv_heads + h0) * D;
     const size_t src = ((size_t)tok * a.num_kv_heads + h0) * D;
@@ -162,6 +173,8 @@ __global__ void __launch_bounds__(256) kv_write_rope_kernel(KvRopeArgs a) {
 }
 
 }  // namespace
+
+PA_DEFINE_TAKE_BAD_METADATA(take_bad_metadata_kv_write_rope, g_bad_metadata_kv_write_rope)
 
 hipError_t launch_kv_write_rope(const KvRopeArgs& a, int kv_dtype, hipStream_t stream) {
     const int64_t units = a.head_dim / 8;

@@ -47,6 +47,10 @@
 #include "common.h"
 
 namespace pa {
+
+// Checked build: set when a descriptor or a page id of a segment's key range is out of range.
+__device__ int g_bad_metadata_prefill;
+
 namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -291,6 +295,14 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     const int a0 = dsc[2];
     const int ti = dsc[3];
     const int cap = a.max_pages << a.page_shift;
+    if constexpr (kChecked) {
+        // A non-empty segment lies inside the packed rows, its positions inside the table's
+        // capacity, and its table row exists; a negative length is malformed.
+        if (threadIdx.x == 0 && blockIdx.x == 0 &&
+            (len < 0 || (len > 0 && (start < 0 || len > a.total_tokens - start || a0 < 0 ||
+                                     len > cap - a0 || ti < 0 || ti >= a.num_tables))))
+            mark_bad(&g_bad_metadata_prefill);
+    }
     if (start < 0 || start >= a.total_tokens || len <= 0 || a0 < 0 || a0 >= cap || ti < 0 ||
         ti >= a.num_tables)
         return;
@@ -387,8 +399,11 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     for (pg0 = 0; pg0 <= last_pg; pg0 += kTablePages) {
         const int n = min(kTablePages, last_pg - pg0 + 1);
         if (pg0 > 0) __syncthreads();  // every wave is done with the previous slice
-        for (int i = threadIdx.x; i < n; i += kWaves * 64)
-            s_tbl[i] = clampi(trow[pg0 + i], 0, a.num_pages - 1);
+        for (int i = threadIdx.x; i < n; i += kWaves * 64) {
+            const int v = trow[pg0 + i];
+            if (v < 0 || v >= a.num_pages) mark_bad(&g_bad_metadata_prefill);
+            s_tbl[i] = clampi(v, 0, a.num_pages - 1);
+        }
         __syncthreads();
         khi = min(kmax, ((pg0 + n) << pshift) - 1);
         // A slice starts on a tile boundary: kTablePages pages hold a multiple of 32 keys.
@@ -433,6 +448,8 @@ hipError_t launch_typed(const PrefillArgs& a, int q_blocks, hipStream_t stream) 
 }
 
 }  // namespace
+
+PA_DEFINE_TAKE_BAD_METADATA(take_bad_metadata_prefill, g_bad_metadata_prefill)
 
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int q_blocks,
                           hipStream_t stream) {

@@ -34,13 +34,15 @@ def test_header_lists_the_four_entry_points():
     assert set(names) == set(pa.C_FUNCTIONS)
 
 
-def test_library_exports_every_declared_symbol():
-    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+@pytest.mark.parametrize("checked", [False, True], ids=["product", "checked"])
+def test_library_exports_every_declared_symbol(checked):
+    path = pa.CHECKED_LIB_PATH if checked else pa.LIB_PATH
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     missing = [n for n in header_functions() if n not in exported]
     assert not missing, missing
-    lib = pa.raw_library()
+    lib = pa.raw_library(checked=checked)
     for n in header_functions():
         assert hasattr(lib, n)
 
@@ -50,6 +52,7 @@ def test_status_strings():
     assert pa.paged_attn_status_string(-1) == "invalid argument"
     assert pa.paged_attn_status_string(-2) == "unsupported configuration"
     assert pa.paged_attn_status_string(-3) == "kernel launch failed"
+    assert pa.paged_attn_status_string(-4) == "device metadata out of range (checked build)"
     assert pa.paged_attn_status_string(42) == "unknown status"
 
 
