@@ -59,8 +59,11 @@ def build(verbose: bool = False, extra_flags=(), checked: bool = False) -> str:
 
 
 def build_all(verbose: bool = False):
-    """Both libraries: the product and its checked variant."""
-    return build(verbose), build(verbose, checked=True)
+    """Both libraries, the product and its checked variant, built concurrently."""
+    with cf.ThreadPoolExecutor(2) as ex:
+        product = ex.submit(build, verbose)
+        checked = ex.submit(build, verbose, (), True)
+        return product.result(), checked.result()
 
 
 if __name__ == "__main__":
