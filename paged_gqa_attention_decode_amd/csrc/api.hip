@@ -6,7 +6,9 @@
 // results": malformed shapes, overflow and bad indices are rejected before device access).
 // Device-resident metadata is not read here: that would need a device-to-host copy and a
 // synchronisation.  The kernels instead keep every access inside the buffers the host
-// arguments describe (clamped page ids, clamped lengths, skipped rows).
+// arguments describe (clamped page ids, clamped lengths, skipped rows).  The checked build
+// (-DPAGED_ATTN_CHECKED) is the exception: after each launch it synchronises the stream and
+// reports the metadata its kernels found out of range as PA_EDATA.
 #include <math.h>
 #include <stdint.h>
 

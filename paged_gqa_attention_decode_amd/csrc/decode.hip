@@ -30,6 +30,17 @@
 //         clamped into [0, num_pages) as they are staged.
 //   merge every stream leaves (m, l, O) in LDS; the workgroup writes the split's (m, l) in
 //         natural-log units and the unnormalised O.
+//   step  the single-launch step (paged_attn_decode_fused) also stores the current token's
+//         K/V into its page and merges: the partials leave by device-scope stores, one
+//         relaxed device-scope ticket per (sequence, KV head, head group) finds the last
+//         workgroup, and that one reloads the group's partials and merges them with the
+//         arithmetic of the separate merge kernel, so both paths give the same bits.
+//   heads at most 8 query heads per workgroup (4 at head_dim 256); the host spreads a KV
+//         head's query heads over twice the workgroups when the grid would leave CUs idle
+//         (every grouping sums in the same order).
+//   window with a sliding window W the splits partition the attended positions
+//         [ctx - W, ctx) (vllm.cpp PR #383 names the windowed arm of the decode kernel).
+//   checks the checked build also marks a length or an attended page id out of range.
 #include <algorithm>
 #include <type_traits>
 

@@ -44,6 +44,8 @@
 //   keys  Keys past the block's last visible position are clamped onto it (no branch around
 //         a load); keys past a row's own position are masked to -inf before the
 //         exponential, so their weight is exactly zero.
+//   checks The checked build also marks a malformed descriptor or a staged page id out of
+//         range (every build clamps the page ids and skips the descriptor).
 #include "common.h"
 
 namespace pa {
