@@ -139,3 +139,29 @@ def test_prefill_metadata(checked):
     _expect_edata(lambda: _prefill(c, table=table), "page id")
     pa.use_checked_library(False)
     _prefill(c, table=table)                           # the product library clamps: OK
+
+
+DECODE_NAMES = [n for n, w in wl.WORKLOADS.items() if w.kind == "decode"]
+PREFILL_NAMES = [n for n, w in wl.WORKLOADS.items() if w.kind == "prefill"]
+
+
+@pytest.mark.parametrize("name", DECODE_NAMES + PREFILL_NAMES)
+def test_named_workloads_raise_nothing(checked, name):
+    """Valid metadata never trips a check: every named workload at full size runs through the
+    checked build (write, split partials, merge, and the single-launch step; or the prefill)
+    and gives the product library's bits."""
+    announce(f"checked build: named workload {name}")
+    w = wl.WORKLOADS[name]
+    if w.kind == "decode":
+        case = wl.workload_decode_case(w)
+        got = (DecodeRun(case).step(), DecodeRun(case).fused_step())
+        pa.use_checked_library(False)
+        ref = (DecodeRun(case).step(), DecodeRun(case).fused_step())
+    else:
+        c = wl.workload_prefill_case(w)
+        got = (_prefill(c),)
+        pa.use_checked_library(False)
+        ref = (_prefill(c),)
+    pa.use_checked_library(True)
+    for g, r in zip(got, ref):
+        assert_bitwise(g, r, f"{name}: checked vs product")
