@@ -52,7 +52,8 @@ def check_partials(run, case, kp, vp):
 
 @pytest.mark.parametrize("dtype,ps,hkv,d", [("f32", 16, 12, 64), ("f16", 16, 8, 128),
                                              ("bf16", 32, 8, 128), ("f32", 1, 2, 128),
-                                             ("bf16", 4096, 1, 64)])
+                                             ("bf16", 4096, 1, 64), ("f16", 16, 8, 256),
+                                             ("f32", 8, 4, 256)])
 def test_kv_page_write_bit_exact(dtype, ps, hkv, d):
     announce(f"kv_page_write {dtype} ps={ps} hkv={hkv} d={d}")
     rng = wl.rng_for([200, ps, hkv, d])
@@ -313,6 +314,8 @@ PREFILL_CASES = [
     (8, 8, 64, 1, "f16", [5, 0], [20, 33], 2),
     (12, 4, 128, 32, "f16", [0, 2000], [200, 40], 3),
     (8, 2, 128, 16, "bf16", [16400, 0], [64, 31], 0),   # key range past one page-id slice
+    (12, 3, 64, 256, "f32", [300, 0], [100, 257], 0),   # large pages
+    (8, 4, 128, 4096, "bf16", [5000, 0], [40, 70], 1),  # the largest page size
 ]
 
 

@@ -79,6 +79,7 @@ CASES = [
     ("batch16_64x8_d128_bf16", 16, 64, 8, 128, 32, "bf16", 4080),
     ("chunk_at_70000_28x4_d128_bf16", 96, 28, 4, 128, 16, "bf16", 70001),
     ("no_query_8x2_d64_f16", 40, 0, 2, 64, 1, "f16", 12345),
+    ("d256_16x8_bf16", 24, 16, 8, 256, 16, "bf16", 4000),
 ]
 
 
