@@ -144,7 +144,8 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
  *                   partials)
  *   counters        paged_attn_decode_fused_counters(...) uint32, device: zero before the
  *                   first call; every call leaves them zero again (the last split of a group
- *                   resets its counter), so the buffer is reused without clearing.  One
+ *                   resets its counter; with num_splits = 1 they are not touched), so the
+ *                   buffer is reused without clearing.  One
  *                   counter per (sequence, KV head, group of up to 8 query heads, 4 at
  *                   head_dim 256).
  *   out             [num_seqs][num_q_heads][head_dim] f32, device, written

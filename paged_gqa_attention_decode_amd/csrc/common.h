@@ -146,6 +146,19 @@ struct CoherentPartials {
     }
 };
 
+// A single split's partial held in registers: the source of the merge when a launch has one
+// split, so that its output is the merge's arithmetic on that one partial.
+struct OwnPartial {
+    float2 ml;
+    float4 o;
+    __device__ __forceinline__ float2 ml_at(int s, int S) const {
+        return (s < S) ? ml : make_float2(-INFINITY, 0.f);
+    }
+    __device__ __forceinline__ float4 o_at(int s, int S) const {
+        return (s < S) ? o : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+};
+
 // Merge of one (sequence, head) row's split partials for one float4 column of the output.
 // One pass with a running maximum: every load of a chunk is issued before any of its values
 // is used, so a chunk costs one memory round trip.  Idle splits (l_s = 0) contribute nothing,

@@ -34,7 +34,9 @@
 //         K/V into its page and merges: the partials leave by device-scope stores, one
 //         relaxed device-scope ticket per (sequence, KV head, head group) finds the last
 //         workgroup, and that one reloads the group's partials and merges them with the
-//         arithmetic of the separate merge kernel, so both paths give the same bits.
+//         arithmetic of the separate merge kernel, so both paths give the same bits.  With
+//         one split there is nothing to gather: each workgroup stores its partial, applies
+//         that arithmetic to it in registers and writes the output, with no ticket.
 //   heads at most 8 query heads per workgroup (4 at head_dim 256); the host spreads a KV
 //         head's query heads over twice the workgroups when the grid would leave CUs idle
 //         (every grouping sums in the same order).
@@ -628,53 +630,71 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         pst.ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.partial_ml + row0 * S * 2, 0,
                                                         nh * S * 8, kRawBufferWord3);
     }
-    for (int idx = tid; idx < GH * D4; idx += nthreads) {
-        const int j = idx / D4;
-        const int c = idx - j * D4;
-        if (j >= nh) continue;
-        const float4* t4 = reinterpret_cast<const float4*>(s_t + j * streams);
-        const float4* m4 = reinterpret_cast<const float4*>(s_m + j * streams);
-        const float4* l4 = reinterpret_cast<const float4*>(s_l + j * streams);
-        float M = -INFINITY;
-        for (int q = 0; q < nwaves; ++q) {
-            const float4 v = t4[q];
-            M = fmaxf(M, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
-        }
-        const float ms = (M == -INFINITY) ? 0.f : M;
-        float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-        float L = 0.f;
-        for (int q = 0; q < nwaves; ++q) {
-            const float4 mq = m4[q];
-            const float4 lq = l4[q];
-            const float f[4] = {fast_exp2(mq.x - ms), fast_exp2(mq.y - ms),
-                                fast_exp2(mq.z - ms), fast_exp2(mq.w - ms)};
-            const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
-            float4 v[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                v[k] = *reinterpret_cast<const float4*>(s_o + (4 * q + k) * SOS + j * D + 4 * c);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                O.x = fmaf(v[k].x, f[k], O.x);
-                O.y = fmaf(v[k].y, f[k], O.y);
-                O.z = fmaf(v[k].z, f[k], O.z);
-                O.w = fmaf(v[k].w, f[k], O.w);
-                L = fmaf(lv[k], f[k], L);
+    auto merge_streams = [&](auto emit) {
+        for (int idx = tid; idx < GH * D4; idx += nthreads) {
+            const int j = idx / D4;
+            const int c = idx - j * D4;
+            if (j >= nh) continue;
+            const float4* t4 = reinterpret_cast<const float4*>(s_t + j * streams);
+            const float4* m4 = reinterpret_cast<const float4*>(s_m + j * streams);
+            const float4* l4 = reinterpret_cast<const float4*>(s_l + j * streams);
+            float M = -INFINITY;
+            for (int q = 0; q < nwaves; ++q) {
+                const float4 v = t4[q];
+                M = fmaxf(M, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
             }
+            const float ms = (M == -INFINITY) ? 0.f : M;
+            float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+            float L = 0.f;
+            for (int q = 0; q < nwaves; ++q) {
+                const float4 mq = m4[q];
+                const float4 lq = l4[q];
+                const float f[4] = {fast_exp2(mq.x - ms), fast_exp2(mq.y - ms),
+                                    fast_exp2(mq.z - ms), fast_exp2(mq.w - ms)};
+                const float lv[4] = {lq.x, lq.y, lq.z, lq.w};
+                float4 v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    v[k] = *reinterpret_cast<const float4*>(s_o + (4 * q + k) * SOS + j * D +
+                                                            4 * c);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    O.x = fmaf(v[k].x, f[k], O.x);
+                    O.y = fmaf(v[k].y, f[k], O.y);
+                    O.z = fmaf(v[k].z, f[k], O.z);
+                    O.w = fmaf(v[k].w, f[k], O.w);
+                    L = fmaf(lv[k], f[k], L);
+                }
+            }
+            const float mo = (L > 0.f) ? M * kLn2 : -INFINITY;
+            emit(j, c, O, mo, L);
         }
-        const float mo = (L > 0.f) ? M * kLn2 : -INFINITY;
-        if constexpr (FUSED) {
-            const uint32_t js = (uint32_t)(j * S + split);
-            pst.o(js * (uint32_t)(D * 4) + (uint32_t)c * 16u, O);
-            if (c == 0) pst.ml(js * 8u, mo, L);
-        } else {
+    };
+
+    if constexpr (!FUSED) {
+        merge_streams([&](int j, int c, float4 O, float mo, float L) {
             const size_t slot = ((size_t)b * a.num_q_heads + h0 + j) * S + split;
             reinterpret_cast<float4*>(a.partial_o + slot * D)[c] = O;
             if (c == 0) reinterpret_cast<float2*>(a.partial_ml)[slot] = make_float2(mo, L);
+        });
+    } else {
+        auto store_partial = [&](int j, int c, float4 O, float mo, float L) {
+            const uint32_t js = (uint32_t)(j * S + split);
+            pst.o(js * (uint32_t)(D * 4) + (uint32_t)c * 16u, O);
+            if (c == 0) pst.ml(js * 8u, mo, L);
+        };
+        if (S == 1) {
+            // One split: this partial is the whole row, and the merge's arithmetic applied to
+            // it in registers gives the output the separate merge computes.  No ticket; the
+            // counter stays at zero.
+            merge_streams([&](int j, int c, float4 O, float mo, float L) {
+                store_partial(j, c, O, mo, L);
+                reinterpret_cast<float4*>(a.out)[((size_t)b * a.num_q_heads + h0 + j) * D4 + c] =
+                    merge_splits(OwnPartial{make_float2(mo, L), O}, 1);
+            });
+            return;
         }
-    }
-
-    if constexpr (FUSED) {
+        merge_streams(store_partial);
         // The last of the group's S workgroups to finish merges their partials.  The partials
         // travel by device-scope stores and loads (written through to, and read from, the
         // device's coherence point), so no fence has to write back or invalidate a whole L2

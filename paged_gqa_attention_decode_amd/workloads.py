@@ -79,7 +79,7 @@ def rng_for(case_id) -> np.random.Generator:
 
 
 def named_rng(index: int) -> np.random.Generator:
-    ss = np.random.SeedSequence(MASTER_SEED).spawn(8)[index]   # child i does not depend on n
+    ss = np.random.SeedSequence(MASTER_SEED).spawn(9)[index]   # child i does not depend on n
     return np.random.Generator(np.random.PCG64(ss))
 
 
@@ -157,6 +157,13 @@ WORKLOADS = {
         name="prefill_hq12_hkv3_d64_t512_bf16", kind="prefill", index=7, hq=12, hkv=3,
         head_dim=64, page_size=16, dtype="bf16", tokens=512, num_pages=32, scale=0.125,
         description="causal packed prefill of one 512-token sequence, GQA 12/3, bf16 pool"),
+    # The 14B decode shape at a serving batch of 128: 1.7 GB of K/V per layer, several times
+    # the last-level cache, so the step streams from HBM.  A throughput shape beside the
+    # batch-1 one (same recipe; one split per sequence fills the device).
+    "decode_b128_hq40_hkv8_d128_ctx3254_f16": Workload(
+        name="decode_b128_hq40_hkv8_d128_ctx3254_f16", kind="decode", index=8, hq=40, hkv=8,
+        head_dim=128, page_size=16, dtype="f16", batch=128, ctx=(3254,) * 128,
+        num_splits=1, description="14B-shape decode, batch 128 sequences of 3254 positions"),
 }
 
 
