@@ -16,7 +16,9 @@
 //         resident at once (occupancy, not a second register set, hides the load latency).
 //         The causal key range of the block is cut into 32-key tiles dealt round-robin to
 //         the 8 waves, starting at a block-dependent wave; the 8 partial softmax states
-//         merge through LDS at the end.  The page ids of the block's key range are staged in
+//         merge through LDS at the end.  With a 16-bit pool a wave requests its next tile's
+//         K once the scores have used the current K, and its V once the PV product has used
+//         the current V.  The page ids of the block's key range are staged in
 //         LDS, 1024 at a time.
 //   math  Scores are computed transposed, S^T = K * Q^T (16 keys x 16 rows per MFMA), so
 //         each lane ends with 4 keys of ONE query row (row = lane % 16).  That register
@@ -46,6 +48,8 @@
 //         exponential, so their weight is exactly zero.
 //   checks The checked build also marks a malformed descriptor or a staged page id out of
 //         range (every build clamps the page ids and skips the descriptor).
+#include <type_traits>
+
 #include "common.h"
 
 namespace pa {
@@ -126,9 +130,8 @@ struct Operands<F32, D> {
     }
 
     template <class RowOff>
-    __device__ __forceinline__ static void load_tile(Tile& tl, const float* kp, const float* vp,
-                                                     RowOff row_off, int j0, int khi, int g,
-                                                     int c16) {
+    __device__ __forceinline__ static void load_k(Tile& tl, const float* kp, RowOff row_off,
+                                                  int j0, int khi, int g, int c16) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const float* kr = kp + row_off(min(j0 + 16 * st + c16, khi)) + 4 * g;
@@ -140,6 +143,13 @@ struct Operands<F32, D> {
                 tl.kf[st][c][2] = t.z;
                 tl.kf[st][c][3] = t.w;
             }
+        }
+    }
+    template <class RowOff>
+    __device__ __forceinline__ static void load_v(Tile& tl, const float* vp, RowOff row_off,
+                                                  int j0, int khi, int g, int c16) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float* vr = vp + row_off(min(j0 + 16 * st + 4 * g + i, khi)) + NC * c16;
@@ -152,7 +162,6 @@ struct Operands<F32, D> {
                     tl.vf[st][i][d4 + 3] = t.w;
                 }
             }
-        }
     }
 
     // S^T = K Q^T: lane (g, c16) gets the scores of keys j0 + 16 st + 4g + i for row c16.
@@ -209,14 +218,20 @@ struct Operands {
     }
 
     template <class RowOff>
-    __device__ __forceinline__ static void load_tile(Tile& tl, const T* kp, const T* vp,
-                                                     RowOff row_off, int j0, int khi, int g,
-                                                     int c16) {
+    __device__ __forceinline__ static void load_k(Tile& tl, const T* kp, RowOff row_off, int j0,
+                                                  int khi, int g, int c16) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const T* kr = kp + row_off(min(j0 + 16 * st + c16, khi)) + 8 * g;
 #pragma unroll
             for (int c = 0; c < NK; ++c) tl.k[st][c] = *reinterpret_cast<const uint4*>(kr + 32 * c);
+        }
+    }
+    template <class RowOff>
+    __device__ __forceinline__ static void load_v(Tile& tl, const T* vp, RowOff row_off, int j0,
+                                                  int khi, int g, int c16) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const T* vr = vp + row_off(min(j0 + 16 * st + 4 * g + i, khi)) + NC * c16;
@@ -235,7 +250,6 @@ struct Operands {
                     }
                 }
             }
-        }
     }
 
     __device__ __forceinline__ void scores(const Tile& tl, floatx4 (&sacc)[2]) const {
@@ -349,10 +363,12 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     // Keys past khi are clamped onto khi (a valid row, so no branch guards a load: the wait
     // for the current tile then never covers the loads of the next one).  Only the last
     // slice has such keys (khi = kmax there); their scores are masked for every row.
-    auto compute_tile = [&](const typename Ops::Tile& tl, int t) {
+    auto compute_tile = [&](const typename Ops::Tile& tl, int t, auto after_scores,
+                            auto after_pv) {
         const int j0 = t * kTileKeys;
         floatx4 sacc[2];
         ops.scores(tl, sacc);
+        after_scores();
 
         float tmax = -INFINITY;
         float s[2][4];
@@ -382,6 +398,7 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
 #pragma unroll
         for (int dt = 0; dt < NC; ++dt) oacc[dt] *= alpha;
         Ops::pv(tl, p, oacc);
+        after_pv();
     };
 
     // This wave's tiles of a slice: t = t0 + w, t0 + w + 8, ... with w = (wave + block) % 8,
@@ -389,11 +406,39 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     // instead of all reading tile t0 at once.  The rotation depends only on the block's own
     // first row, so a segment computes the same bits wherever it sits in the packed batch.
     const int first = (wave + (r0 / kRows)) % kWaves;
+    // 16-bit pools: the next tile's K is requested as soon as the scores have consumed this
+    // tile's K, and its V once the PV product has consumed this tile's V, so the loads overlap
+    // the softmax and the PV product without a second tile's worth of live registers.  Past
+    // the wave's last tile the requests go on unguarded (keys clamp onto khi: cache hits,
+    // never used), since a load guarded by a branch makes the compiler's wait counts assume
+    // the path without it, and a counted, peeled schedule keeps two tiles live and spills.
+    // The f32 pool keeps one tile in flight: its tiles are twice the bytes, its MFMA pipe is
+    // already the shared resource, and the early requests measured slower there.
     auto run_tiles = [&](int t, int t_end) {
-        for (; t < t_end; t += kWaves) {
-            typename Ops::Tile tl;
-            Ops::load_tile(tl, kp, vp, row_off, t * kTileKeys, khi, g, c16);
-            compute_tile(tl, t);
+        if constexpr (std::is_same_v<KV, F32>) {
+            for (; t < t_end; t += kWaves) {
+                typename Ops::Tile tl;
+                Ops::load_k(tl, kp, row_off, t * kTileKeys, khi, g, c16);
+                Ops::load_v(tl, vp, row_off, t * kTileKeys, khi, g, c16);
+                compute_tile(tl, t, [] {}, [] {});
+            }
+        } else {
+            if (t >= t_end) return;
+            typename Ops::Tile A, B;
+            Ops::load_k(A, kp, row_off, t * kTileKeys, khi, g, c16);
+            Ops::load_v(A, vp, row_off, t * kTileKeys, khi, g, c16);
+            for (;;) {
+                int jn = (t + kWaves) * kTileKeys;
+                compute_tile(A, t, [&] { Ops::load_k(B, kp, row_off, jn, khi, g, c16); },
+                             [&] { Ops::load_v(B, vp, row_off, jn, khi, g, c16); });
+                t += kWaves;
+                if (t >= t_end) break;
+                jn = (t + kWaves) * kTileKeys;
+                compute_tile(B, t, [&] { Ops::load_k(A, kp, row_off, jn, khi, g, c16); },
+                             [&] { Ops::load_v(A, vp, row_off, jn, khi, g, c16); });
+                t += kWaves;
+                if (t >= t_end) break;
+            }
         }
     };
 
