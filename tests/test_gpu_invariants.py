@@ -159,7 +159,8 @@ def test_prefill_segment_isolation_bitwise():
         assert_bitwise(run(alone), full[rows], f"segment {i} alone vs packed")
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,d,S", [("f16", 40, 8, 128, 32), ("f32", 12, 3, 64, 7)])
+@pytest.mark.parametrize("dtype,hq,hkv,d,S", [("f16", 40, 8, 128, 32), ("f32", 12, 3, 64, 7),
+                                              ("bf16", 64, 8, 128, 1)])
 def test_empty_sequences_in_a_batch(dtype, hq, hkv, d, S):
     """Sequences of context 0 (free slots of a continuous batch) give zero rows and idle
     partials; the other rows are those of the same batch without them, bit for bit; the

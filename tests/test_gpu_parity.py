@@ -221,6 +221,23 @@ def test_decode_fused_workload(name):
     _fused_checks(case, what=name)
 
 
+@pytest.mark.parametrize("geom", [(40, 8, 128, 16, "f16", 0, [3254, 1, 700]),
+                                  (64, 8, 128, 32, "bf16", 0, [2000, 33, 4096]),
+                                  (8, 2, 64, 16, "f32", 0, [256, 17]),
+                                  (16, 8, 256, 16, "bf16", 0, [1500, 64]),
+                                  (28, 4, 128, 16, "f16", 100, [1641, 99, 101])])
+def test_decode_fused_one_split(geom):
+    """One split per sequence: each workgroup of the single-launch step writes the output
+    from its own partial, with no ticket.  Same bars as every single-launch check (oracle,
+    three-launch bits, pool bits, counters at zero, repeat call, partials)."""
+    hq, hkv, d, ps, dtype, window, ctx = geom
+    announce(f"fused decode S=1 {geom}")
+    rng = wl.rng_for([330, hq, d, window])
+    case = wl.make_decode_case(rng, batch=len(ctx), hq=hq, hkv=hkv, head_dim=d, page_size=ps,
+                               dtype=dtype, ctx=ctx, num_splits=1, window=window)
+    _fused_checks(case, S=1, what=f"S=1 {geom}")
+
+
 @pytest.mark.parametrize("splits", [1, 3, 64, 4096])
 def test_decode_fused_split_counts(splits):
     case = wl.workload_decode_case(wl.WORKLOADS["decode_hq28_hkv4_d128_ctx1641_f16"])
