@@ -368,3 +368,41 @@ def test_prefill_cases(c):
     covered = case.token_table_index >= 0
     assert np.all(got[~covered] == 7.0), "rows outside every segment must stay untouched"
     assert_within(got[covered], ref[covered], *tolerance(dtype), f"prefill {c}")
+
+
+# ----------------------------------------------------------------------------- largest grids
+
+MAX_GRID_Z = 65535   # sequences per decode call, segments per prefill call
+
+
+def test_decode_largest_batch():
+    """The largest batch a decode call takes (65,535 sequences, one per grid row), with
+    short contexts: every row against the oracle, the page write bit-exact, and the
+    single-launch step (131,070 counters) bit-identical to the three launches."""
+    announce("decode, 65535 sequences")
+    rng = wl.rng_for(340)
+    ctx = [int(x) for x in rng.integers(1, 9, size=MAX_GRID_Z)]
+    case = wl.make_decode_case(rng, batch=MAX_GRID_Z, hq=2, hkv=1, head_dim=64, page_size=4,
+                               dtype="f16", ctx=ctx, num_splits=2)
+    run = DecodeRun(case)
+    out = run.step()
+    kp, vp, ref = oracle_step(case)
+    assert_bitwise(host(run.kp), kp, "K pool after write")
+    assert_within(out, ref, *tolerance("f16"), "decode, 65535 sequences")
+    fused = DecodeRun(case)
+    assert_bitwise(fused.fused_step(), out, "single launch vs three launches")
+    assert int(fused.counters.abs().sum().item()) == 0, "counters must be left at zero"
+
+
+def test_prefill_most_segments():
+    """The most segments a prefill call takes (65,535, one per grid row), one packed row
+    each over a history of 0-7 positions, against the oracle."""
+    announce("prefill, 65535 segments")
+    rng = wl.rng_for(341)
+    starts = [int(x) for x in rng.integers(0, 8, size=MAX_GRID_Z)]
+    case = wl.make_prefill_case(rng, hq=2, hkv=1, head_dim=64, page_size=4, dtype="bf16",
+                                lens=[1] * MAX_GRID_Z, starts=starts)
+    got, gk, _ = run_prefill(case)
+    ref, rk, _, _ = oracle_prefill(case)
+    assert_bitwise(gk, rk, "K pool after write")
+    assert_within(got, ref, *tolerance("bf16"), "prefill, 65535 segments")
