@@ -406,3 +406,33 @@ def test_prefill_most_segments():
     ref, rk, _, _ = oracle_prefill(case)
     assert_bitwise(gk, rk, "K pool after write")
     assert_within(got, ref, *tolerance("bf16"), "prefill, 65535 segments")
+
+
+def test_decode_million_positions():
+    """One sequence of 2^20 positions (65,536 pages of 16, the table staged in many LDS
+    slices, 64 splits of 16,384 rows): output and partials against the oracle, and the
+    single-launch step bit-identical to the three launches."""
+    announce("decode, 2^20 positions")
+    rng = wl.rng_for(342)
+    case = wl.make_decode_case(rng, batch=1, hq=4, hkv=1, head_dim=128, page_size=16,
+                               dtype="bf16", ctx=[1 << 20], num_splits=64)
+    run = DecodeRun(case)
+    out = run.step()
+    kp, vp, ref = oracle_step(case)
+    assert_within(out, ref, *tolerance("bf16"), "decode, 2^20 positions")
+    check_partials(run, case, kp, vp)
+    fused = DecodeRun(case)
+    assert_bitwise(fused.fused_step(), out, "single launch vs three launches")
+
+
+def test_prefill_million_history():
+    """Four packed rows at absolute positions 2^20 - 4 ... 2^20 - 1: every row sees a
+    history of about a million keys over 65,536 pages (64 slices of staged page ids)."""
+    announce("prefill, 2^20-position history")
+    rng = wl.rng_for(343)
+    case = wl.make_prefill_case(rng, hq=2, hkv=1, head_dim=64, page_size=16, dtype="f16",
+                                lens=[4], starts=[(1 << 20) - 4])
+    got, gk, _ = run_prefill(case)
+    ref, rk, _, _ = oracle_prefill(case)
+    assert_bitwise(gk, rk, "K pool after write")
+    assert_within(got, ref, *tolerance("f16"), "prefill, 2^20-position history")
