@@ -111,6 +111,11 @@ def _dev(t, name, dtype=None, ndim=None):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device (HIP) tensor")
+    if t.device.index != torch.cuda.current_device():
+        # The library launches on the current device (its stream, its CU count).
+        raise ValueError(f"{name} is on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}; call under "
+                         f"torch.cuda.device({t.device.index})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
