@@ -32,9 +32,9 @@ int max_heads_per_wg(int head_dim) { return head_dim > 128 ? 4 : kMaxHeadsPerWg;
 
 // Compute units of the current device, read once per device (0 if the runtime cannot say).
 int compute_units() {
-    static std::atomic<int> cached[64] = {};
+    static std::atomic<int> cached[pa::kMaxDevices] = {};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= pa::kMaxDevices) return 0;
     int n = cached[dev].load(std::memory_order_relaxed);
     if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

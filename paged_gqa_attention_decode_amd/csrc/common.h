@@ -11,6 +11,7 @@ namespace pa {
 
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e): scores are kept in base-2 units
 constexpr float kLn2 = 0.6931471805599453f;    // ln(2): back to natural-log units on store
+constexpr int kMaxDevices = 64;  // devices whose host-side launch facts are cached
 
 // ---------------------------------------------------------------- checked build
 

@@ -44,6 +44,7 @@
 //         [ctx - W, ctx) (vllm.cpp PR #383 names the windowed arm of the decode kernel).
 //   checks the checked build also marks a length or an attended page id out of range.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -758,13 +759,22 @@ template <typename KV, int D, int GH, bool FUSED>
 hipError_t launch_gh(const DecodeArgs& a, int waves, hipStream_t stream) {
     using G = DecodeGeom<KV, D>;
     const size_t lds = decode_lds_bytes(waves * kRowsPerLoad, GH, D);
-    // Workgroups asking for more than 64 KB of LDS opt in once per instantiation.
-    static size_t opted = 64 * 1024;
-    if (lds > opted) {
-        hipError_t e = hipFuncSetAttribute(decode_kernel_ptr<KV, D, GH, FUSED>(),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        opted = lds;
+    // Workgroups asking for more than 64 KB of LDS opt in, once per instantiation and device
+    // (the largest size granted so far is kept per device; a repeated grant is harmless).
+    if (lds > 64 * 1024) {
+        static std::atomic<size_t> opted[kMaxDevices] = {};
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+            return hipErrorInvalidDevice;
+        if (lds > opted[dev].load(std::memory_order_relaxed)) {
+            hipError_t e = hipFuncSetAttribute(decode_kernel_ptr<KV, D, GH, FUSED>(),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+            if (e != hipSuccess) return e;
+            size_t cur = opted[dev].load(std::memory_order_relaxed);
+            while (cur < lds && !opted[dev].compare_exchange_weak(cur, lds)) {
+            }
+        }
     }
     const dim3 grid(a.num_splits, a.num_kv_heads * a.head_groups, a.num_seqs);
     if constexpr (FUSED)
