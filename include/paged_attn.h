@@ -48,7 +48,9 @@
  *     a call reads or writes, a malformed prefill descriptor, a write to a missing table row
  *     or beyond the table's capacity (a negative owner or position remains an explicit
  *     skip).  Each call then synchronises its stream and returns PA_EDATA if anything was
- *     recorded.  It is a debugging aid: it synchronises, so it is not for graph capture.
+ *     recorded.  It is a debugging aid: it synchronises, so it is not for graph capture,
+ *     and its records are per library and device, so calls running at the same time from
+ *     several host threads can see each other's reports.
  *   - Layouts are dense row-major with the innermost dimension last:
  *       q            [tokens][Hq][D]                    f32
  *       K/V pages    [num_pages][page_size][Hkv][D]     kv_dtype
