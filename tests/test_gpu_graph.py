@@ -29,7 +29,7 @@ def _eager_noise(run):
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,d,S", [("f16", 40, 8, 128, 32), ("bf16", 64, 8, 128, 8),
-                                               ("f32", 8, 2, 64, 16)])
+                                               ("f32", 8, 2, 64, 16), ("f16", 40, 8, 128, 1)])
 def test_decode_fused_step_in_a_graph(dtype, hq, hkv, d, S):
     announce(f"graph: single-launch decode {dtype} {hq}/{hkv} d={d} S={S}")
     rng = wl.rng_for([700, hq, d])
