@@ -120,7 +120,7 @@ class Workload:
 WORKLOADS = {
     "decode_hq8_hkv2_d64_ctx256_f32": Workload(
         name="decode_hq8_hkv2_d64_ctx256_f32", kind="decode", index=0, hq=8, hkv=2,
-        head_dim=64, page_size=16, dtype="f32", ctx=(256,), num_pages=16, num_splits=16,
+        head_dim=64, page_size=16, dtype="f32", ctx=(256,), num_pages=16, num_splits=1,
         scale=0.125,
         description="single-layer paged decode, batch 1, 16 permuted physical pages"),
     "prefill_hq12_hkv12_d64_t512_f32": Workload(
