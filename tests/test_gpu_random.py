@@ -52,7 +52,7 @@ def _prefill_config(i):
                 gap=gap)
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(48))
 def test_random_decode(i):
     c = _decode_config(i)
     announce(f"random decode {i}: {c}")
@@ -74,7 +74,7 @@ def test_random_decode(i):
     assert_bitwise(fused, out, f"random decode {i}: single launch vs three launches")
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(32))
 def test_random_prefill(i):
     c = _prefill_config(i)
     announce(f"random prefill {i}: {c}")
