@@ -24,11 +24,11 @@ constexpr int64_t kI32Max = 2147483647;
 constexpr int kMaxGridYZ = 65535;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxGroup = 64;
-constexpr int kMaxHeadsPerWg = 8;
-
-// Query heads one decode workgroup serves: 8, or 4 at head_dim 256 (q and the accumulators
-// of a lane are heads x D/16 floats each).
-int max_heads_per_wg(int head_dim) { return head_dim > 128 ? 4 : kMaxHeadsPerWg; }
+// Query heads one decode workgroup serves: the 16 columns of a matrix-core block.
+constexpr int kMaxHeadsPerWg = 16;
+// The single-launch step's counter buffer holds 2 * ceil(group / 8) counters per KV head
+// (paged_attn_decode_fused_counters), at least twice the head groups of any grid below.
+constexpr int kCounterHeads = 8;
 
 // Compute units of the current device, read once per device (0 if the runtime cannot say).
 int compute_units() {
@@ -143,22 +143,21 @@ int make_decode_args(const float* q, const void* k_pages, const void* v_pages, i
         (int64_t)num_seqs * num_q_heads * num_splits * head_dim > kI32Max * 4LL)
         return PA_EINVAL;
     const int group = num_q_heads / num_kv_heads;
-    const int max_heads = max_heads_per_wg(head_dim);
-    int head_groups = (group + max_heads - 1) / max_heads;
+    int head_groups = (group + kMaxHeadsPerWg - 1) / kMaxHeadsPerWg;
     // A grid with fewer workgroups than the device has CUs leaves CUs idle: then the query
     // heads of a KV head are spread over twice the workgroups.  Each reads that KV head's
     // rows; workgroups are dealt to the 8 XCDs in turn, so with a split count that is a
     // multiple of 8 the two workgroups of a split share an XCD and the second read mostly hits
-    // its L2.  Every head grouping sums in the same order, so the result is the same to the
-    // bit.  Twice ceil(group / 8) groups is what the single-launch step's counter buffer
-    // holds per KV head.  Workgroups of fewer than 3 heads cost more in duplicated row reads
-    // than they gain (measured: 8/2 heads at context 256 went 8.0 -> 8.4 us with groups of 2;
-    // 28/4 heads at context 1641 went 12.5 -> 12.0 us with groups of 4 and 3).
-    const int cap_groups = 2 * ((group + kMaxHeadsPerWg - 1) / kMaxHeadsPerWg);
+    // its L2.  A head's column gives the same bits in any grouping, so the result is the same
+    // to the bit.  Workgroups of fewer than 3 heads cost more in duplicated row reads than
+    // they gain (measured: 8/2 heads at context 256 went 8.0 -> 8.4 us with groups of 2).
     if ((int64_t)num_seqs * num_kv_heads * head_groups * num_splits < compute_units() &&
-        2 * head_groups <= cap_groups && (group + 2 * head_groups - 1) / (2 * head_groups) >= 3)
+        (group + 2 * head_groups - 1) / (2 * head_groups) >= 3)
         head_groups *= 2;
     const int heads_per_wg = (group + head_groups - 1) / head_groups;
+    // Every head group serves at least one query head (9 heads in 4 groups would be 3, 3, 3
+    // and an empty one): the count follows from the group size.
+    head_groups = (group + heads_per_wg - 1) / heads_per_wg;
     if ((int64_t)num_kv_heads * head_groups > kMaxGridYZ) return PA_EUNSUPPORTED;
 
     pa::DecodeArgs a = {};
@@ -210,8 +209,7 @@ size_t paged_attn_decode_fused_counters(int num_seqs, int num_q_heads, int num_k
     if (num_seqs < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads)
         return 0;
     const int group = num_q_heads / num_kv_heads;
-    const int head_groups = (group + kMaxHeadsPerWg - 1) / kMaxHeadsPerWg;
-    // Enough for head_dim 256 too (at most 4 heads per workgroup there: twice the groups).
+    const int head_groups = (group + kCounterHeads - 1) / kCounterHeads;
     return (size_t)num_seqs * num_kv_heads * head_groups * 2;
 }
 

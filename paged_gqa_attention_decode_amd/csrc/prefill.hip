@@ -50,7 +50,7 @@
 //         range (every build clamps the page ids and skips the descriptor).
 #include <type_traits>
 
-#include "common.h"
+#include "mfma_tiles.h"
 
 namespace pa {
 
@@ -59,238 +59,15 @@ __device__ int g_bad_metadata_prefill;
 
 namespace {
 
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
 constexpr int kWaves = 8;
 constexpr int kRows = 16;         // query rows per workgroup
-constexpr int kTileKeys = 32;     // keys per wave per step (two 16-key MFMA blocks)
 constexpr int kTablePages = 1024; // page ids staged in LDS per slice of the key range
-
-__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma32(F16, uint4 a, uint4 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a),
-                                                   __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx4 mfma32(BF16, uint4 a, uint4 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// x and y each split into hi + lo terms of the 16-bit type (both rounded to nearest even):
-// hi packs (hi(x), hi(y)) and lo packs (lo(x), lo(y)), x in the low half.
-__device__ __forceinline__ void split_pair(F16, float x, float y, uint32_t& hi, uint32_t& lo) {
-    const _Float16 hx = (_Float16)x, hy = (_Float16)y;
-    const _Float16 lx = (_Float16)(x - (float)hx), ly = (_Float16)(y - (float)hy);
-    hi = (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
-    lo = (uint32_t)__builtin_bit_cast(uint16_t, lx) | ((uint32_t)__builtin_bit_cast(uint16_t, ly) << 16);
-}
-__device__ __forceinline__ void split_pair(BF16, float x, float y, uint32_t& hi, uint32_t& lo) {
-    const __bf16 hx = (__bf16)x, hy = (__bf16)y;
-    const __bf16 lx = (__bf16)(x - (float)hx), ly = (__bf16)(y - (float)hy);
-    hi = (uint32_t)__builtin_bit_cast(uint16_t, hx) | ((uint32_t)__builtin_bit_cast(uint16_t, hy) << 16);
-    lo = (uint32_t)__builtin_bit_cast(uint16_t, lx) | ((uint32_t)__builtin_bit_cast(uint16_t, ly) << 16);
-}
-
-// The 16-bit element sel of word a (low half) and of word b (high half), sel 0 or 1.
-__device__ __forceinline__ uint32_t pair_halves(uint32_t a, uint32_t b, int sel) {
-    return __builtin_amdgcn_perm(b, a, sel ? 0x07060302u : 0x05040100u);
-}
-
-// Operands and tile products of one wave.  `row_off(key)` gives a key's element offset
-// within the pool (page translated); kp and vp point at the kv head's dims of slot 0.
-template <typename KV, int D>
-struct Operands;
-
-// f32 K/V on v_mfma_f32_16x16x4_f32.
-template <int D>
-struct Operands<F32, D> {
-    static constexpr int NC = D / 16;
-    // Q^T operand: lane (g, c16) holds Q[row][16c + 4g + kk], kk = 0..3.
-    float q[NC][4];
-    struct Tile {
-        // K operand: lane (g, c16) of block st holds K[j0 + 16 st + c16][16c + 4g + kk].
-        float kf[2][NC][4];
-        // V^T operand of MFMA (st, i, dt): lane (g, c16) holds V[j0 + 16 st + 4g + i][NC c16 + dt].
-        float vf[2][4][NC];
-    };
-
-    __device__ __forceinline__ void load_q(const float* row, float qs, int g) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const float4 t = *reinterpret_cast<const float4*>(row + 16 * c + 4 * g);
-            q[c][0] = t.x * qs;
-            q[c][1] = t.y * qs;
-            q[c][2] = t.z * qs;
-            q[c][3] = t.w * qs;
-        }
-    }
-
-    template <class RowOff>
-    __device__ __forceinline__ static void load_k(Tile& tl, const float* kp, RowOff row_off,
-                                                  int j0, int khi, int g, int c16) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const float* kr = kp + row_off(min(j0 + 16 * st + c16, khi)) + 4 * g;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const float4 t = *reinterpret_cast<const float4*>(kr + 16 * c);
-                tl.kf[st][c][0] = t.x;
-                tl.kf[st][c][1] = t.y;
-                tl.kf[st][c][2] = t.z;
-                tl.kf[st][c][3] = t.w;
-            }
-        }
-    }
-    template <class RowOff>
-    __device__ __forceinline__ static void load_v(Tile& tl, const float* vp, RowOff row_off,
-                                                  int j0, int khi, int g, int c16) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float* vr = vp + row_off(min(j0 + 16 * st + 4 * g + i, khi)) + NC * c16;
-#pragma unroll
-                for (int d4 = 0; d4 < NC; d4 += 4) {
-                    const float4 t = *reinterpret_cast<const float4*>(vr + d4);
-                    tl.vf[st][i][d4 + 0] = t.x;
-                    tl.vf[st][i][d4 + 1] = t.y;
-                    tl.vf[st][i][d4 + 2] = t.z;
-                    tl.vf[st][i][d4 + 3] = t.w;
-                }
-            }
-    }
-
-    // S^T = K Q^T: lane (g, c16) gets the scores of keys j0 + 16 st + 4g + i for row c16.
-    __device__ __forceinline__ void scores(const Tile& tl, floatx4 (&sacc)[2]) const {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            sacc[st] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    sacc[st] = mfma4(tl.kf[st][c][kk], q[c][kk], sacc[st]);
-        }
-    }
-
-    // O^T += V^T P^T (accumulator row c of block dt is output dim NC c + dt).
-    __device__ __forceinline__ static void pv(const Tile& tl, const float (&p)[2][4],
-                                              floatx4 (&oacc)[NC]) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int dt = 0; dt < NC; ++dt)
-                    oacc[dt] = mfma4(tl.vf[st][i][dt], p[st][i], oacc[dt]);
-    }
-};
-
-// f16 / bf16 K/V on v_mfma_f32_16x16x32_{f16,bf16}; Q and P as hi + lo terms.
-template <typename KV, int D>
-struct Operands {
-    static constexpr int NC = D / 16;
-    static constexpr int NK = D / 32;  // 32-dim chunks of a row = 32-bit words of NC dims
-    using T = uint16_t;
-    // Q^T operand terms: lane (g, c16) holds Q[row][32c + 8g + e], e = 0..7.
-    uint4 qh[NK], ql[NK];
-    struct Tile {
-        // K operand of block st: lane (g, c16) holds K[j0 + 16 st + c16][32c + 8g + e].
-        uint4 k[2][NK];
-        // Lane (g, c16): V[j0 + 16 st + 4g + i][NC c16 + 2w + (0, 1)] in word w.
-        uint32_t v[2][4][NK];
-    };
-
-    __device__ __forceinline__ void load_q(const float* row, float qs, int g) {
-#pragma unroll
-        for (int c = 0; c < NK; ++c) {
-            const float4 a = *reinterpret_cast<const float4*>(row + 32 * c + 8 * g);
-            const float4 b = *reinterpret_cast<const float4*>(row + 32 * c + 8 * g + 4);
-            split_pair(KV{}, a.x * qs, a.y * qs, qh[c].x, ql[c].x);
-            split_pair(KV{}, a.z * qs, a.w * qs, qh[c].y, ql[c].y);
-            split_pair(KV{}, b.x * qs, b.y * qs, qh[c].z, ql[c].z);
-            split_pair(KV{}, b.z * qs, b.w * qs, qh[c].w, ql[c].w);
-        }
-    }
-
-    template <class RowOff>
-    __device__ __forceinline__ static void load_k(Tile& tl, const T* kp, RowOff row_off, int j0,
-                                                  int khi, int g, int c16) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const T* kr = kp + row_off(min(j0 + 16 * st + c16, khi)) + 8 * g;
-#pragma unroll
-            for (int c = 0; c < NK; ++c) tl.k[st][c] = *reinterpret_cast<const uint4*>(kr + 32 * c);
-        }
-    }
-    template <class RowOff>
-    __device__ __forceinline__ static void load_v(Tile& tl, const T* vp, RowOff row_off, int j0,
-                                                  int khi, int g, int c16) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const T* vr = vp + row_off(min(j0 + 16 * st + 4 * g + i, khi)) + NC * c16;
-                if constexpr (NK == 2) {
-                    const uint2 t = *reinterpret_cast<const uint2*>(vr);
-                    tl.v[st][i][0] = t.x;
-                    tl.v[st][i][1] = t.y;
-                } else {
-#pragma unroll
-                    for (int w = 0; w < NK; w += 4) {
-                        const uint4 t = *reinterpret_cast<const uint4*>(vr + 2 * w);
-                        tl.v[st][i][w + 0] = t.x;
-                        tl.v[st][i][w + 1] = t.y;
-                        tl.v[st][i][w + 2] = t.z;
-                        tl.v[st][i][w + 3] = t.w;
-                    }
-                }
-            }
-    }
-
-    __device__ __forceinline__ void scores(const Tile& tl, floatx4 (&sacc)[2]) const {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            sacc[st] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NK; ++c) sacc[st] = mfma32(KV{}, tl.k[st][c], qh[c], sacc[st]);
-#pragma unroll
-            for (int c = 0; c < NK; ++c) sacc[st] = mfma32(KV{}, tl.k[st][c], ql[c], sacc[st]);
-        }
-    }
-
-    __device__ __forceinline__ static void pv(const Tile& tl, const float (&p)[2][4],
-                                              floatx4 (&oacc)[NC]) {
-        // P^T operand: element e = p[e / 4][e % 4], as hi and lo terms.
-        uint4 ph, pl;
-        split_pair(KV{}, p[0][0], p[0][1], ph.x, pl.x);
-        split_pair(KV{}, p[0][2], p[0][3], ph.y, pl.y);
-        split_pair(KV{}, p[1][0], p[1][1], ph.z, pl.z);
-        split_pair(KV{}, p[1][2], p[1][3], ph.w, pl.w);
-#pragma unroll
-        for (int dt = 0; dt < NC; ++dt) {
-            // V^T operand of dim block dt: element e = V[key e][NC c16 + dt].
-            const int w = dt >> 1, sel = dt & 1;
-            uint4 va;
-            va.x = pair_halves(tl.v[0][0][w], tl.v[0][1][w], sel);
-            va.y = pair_halves(tl.v[0][2][w], tl.v[0][3][w], sel);
-            va.z = pair_halves(tl.v[1][0][w], tl.v[1][1][w], sel);
-            va.w = pair_halves(tl.v[1][2][w], tl.v[1][3][w], sel);
-            oacc[dt] = mfma32(KV{}, va, ph, oacc[dt]);
-            oacc[dt] = mfma32(KV{}, va, pl, oacc[dt]);
-        }
-    }
-};
 
 template <typename KV, int D>
 __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 4 : 2)))
     prefill_kernel(PrefillArgs a) {
     using T = typename KV::storage;
-    using Ops = Operands<KV, D>;
+    using Ops = TileOps<KV, D>;
     constexpr int NC = D / 16;             // 16-wide dimension blocks
 
     __shared__ int s_tbl[kTablePages];
@@ -353,6 +130,8 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
         const int page = s_tbl[(key >> pshift) - pg0];
         return (((size_t)page << pshift) | (size_t)(key & pmask)) * slot_stride;
     };
+    auto krow = [&](int key) -> const T* { return kp + row_off(key); };
+    auto vrow = [&](int key) -> const T* { return vp + row_off(key); };
 
     float m = -INFINITY;
     float lsum = 0.f;
@@ -418,24 +197,24 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
         if constexpr (std::is_same_v<KV, F32>) {
             for (; t < t_end; t += kWaves) {
                 typename Ops::Tile tl;
-                Ops::load_k(tl, kp, row_off, t * kTileKeys, khi, g, c16);
-                Ops::load_v(tl, vp, row_off, t * kTileKeys, khi, g, c16);
+                Ops::load_k(tl, krow, t * kTileKeys, khi, g, c16);
+                Ops::load_v(tl, vrow, t * kTileKeys, khi, g, c16);
                 compute_tile(tl, t, [] {}, [] {});
             }
         } else {
             if (t >= t_end) return;
             typename Ops::Tile A, B;
-            Ops::load_k(A, kp, row_off, t * kTileKeys, khi, g, c16);
-            Ops::load_v(A, vp, row_off, t * kTileKeys, khi, g, c16);
+            Ops::load_k(A, krow, t * kTileKeys, khi, g, c16);
+            Ops::load_v(A, vrow, t * kTileKeys, khi, g, c16);
             for (;;) {
                 int jn = (t + kWaves) * kTileKeys;
-                compute_tile(A, t, [&] { Ops::load_k(B, kp, row_off, jn, khi, g, c16); },
-                             [&] { Ops::load_v(B, vp, row_off, jn, khi, g, c16); });
+                compute_tile(A, t, [&] { Ops::load_k(B, krow, jn, khi, g, c16); },
+                             [&] { Ops::load_v(B, vrow, jn, khi, g, c16); });
                 t += kWaves;
                 if (t >= t_end) break;
                 jn = (t + kWaves) * kTileKeys;
-                compute_tile(B, t, [&] { Ops::load_k(A, kp, row_off, jn, khi, g, c16); },
-                             [&] { Ops::load_v(A, vp, row_off, jn, khi, g, c16); });
+                compute_tile(B, t, [&] { Ops::load_k(A, krow, jn, khi, g, c16); },
+                             [&] { Ops::load_v(A, vrow, jn, khi, g, c16); });
                 t += kWaves;
                 if (t >= t_end) break;
             }

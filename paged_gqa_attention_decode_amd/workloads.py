@@ -79,7 +79,7 @@ def rng_for(case_id) -> np.random.Generator:
 
 
 def named_rng(index: int) -> np.random.Generator:
-    ss = np.random.SeedSequence(MASTER_SEED).spawn(9)[index]   # child i does not depend on n
+    ss = np.random.SeedSequence(MASTER_SEED).spawn(16)[index]  # child i does not depend on n
     return np.random.Generator(np.random.PCG64(ss))
 
 
@@ -106,6 +106,8 @@ class Workload:
     scale: float = 0.0         # 0: 1/sqrt(head_dim) rounded to f32
     rotations: int = 1         # disjoint page sets the bench cycles through
     window: int = 0            # decode: sliding window in positions (0: whole context)
+    seg_lens: tuple = ()       # prefill: chunk lengths of a multi-segment pack (else `tokens`)
+    seg_starts: tuple = ()     # prefill: absolute start of each segment
     description: str = ""
 
     @property
@@ -131,10 +133,12 @@ WORKLOADS = {
         name="decode_hq40_hkv8_d128_ctx3254_f16", kind="decode", index=2, hq=40, hkv=8,
         head_dim=128, page_size=16, dtype="f16", ctx=(3254,), num_pages=204, num_splits=32,
         layers=48, description="14B-shape decode, batch 1, 48 layers per step"),
+    # Four disjoint page sets per layer pool (4 x 28 x 3.36 MB = 376 MB of K/V, more than the
+    # 256 MB last-level cache), cycled step by step, so the step's K/V comes from HBM.
     "decode_hq28_hkv4_d128_ctx1641_f16": Workload(
         name="decode_hq28_hkv4_d128_ctx1641_f16", kind="decode", index=3, hq=28, hkv=4,
-        head_dim=128, page_size=16, dtype="f16", ctx=(1641,), num_pages=103, num_splits=32,
-        layers=28, description="7B-shape decode, batch 1, 28 layers per step"),
+        head_dim=128, page_size=16, dtype="f16", ctx=(1641,), num_splits=32, layers=28,
+        rotations=4, description="7B-shape decode, batch 1, 28 layers per step"),
     "decode_b16_hq64_hkv8_d128_ctx64to4096_bf16": Workload(
         name="decode_b16_hq64_hkv8_d128_ctx64to4096_bf16", kind="decode", index=4, hq=64,
         hkv=8, head_dim=128, page_size=32, dtype="bf16", batch=16, ctx_range=(64, 4096),
@@ -157,6 +161,24 @@ WORKLOADS = {
         name="prefill_hq12_hkv3_d64_t512_bf16", kind="prefill", index=7, hq=12, hkv=3,
         head_dim=64, page_size=16, dtype="bf16", tokens=512, num_pages=32, scale=0.125,
         description="causal packed prefill of one 512-token sequence, GQA 12/3, bf16 pool"),
+    # The prefill microbenchmark shapes of crucible's results page, in its production GQA
+    # geometry (12 query heads over 3 KV heads, head_dim 64, 16-token pages, f32 pool): one
+    # 512-token request, four 256-token requests, and the heterogeneous pack (starts 0, 63,
+    # 255, 512; lengths 17, 64, 129, 257), each request with its own page table.
+    "prefill_hq12_hkv3_d64_t512_f32": Workload(
+        name="prefill_hq12_hkv3_d64_t512_f32", kind="prefill", index=9, hq=12, hkv=3,
+        head_dim=64, page_size=16, dtype="f32", tokens=512, scale=0.125,
+        description="causal prefill of one 512-token request, GQA 12/3, f32 pool"),
+    "prefill_hq12_hkv3_d64_4x256_f32": Workload(
+        name="prefill_hq12_hkv3_d64_4x256_f32", kind="prefill", index=10, hq=12, hkv=3,
+        head_dim=64, page_size=16, dtype="f32", tokens=1024, seg_lens=(256, 256, 256, 256),
+        seg_starts=(0, 0, 0, 0), scale=0.125,
+        description="causal packed prefill of four 256-token requests, GQA 12/3, f32 pool"),
+    "prefill_hq12_hkv3_d64_hetero_f32": Workload(
+        name="prefill_hq12_hkv3_d64_hetero_f32", kind="prefill", index=11, hq=12, hkv=3,
+        head_dim=64, page_size=16, dtype="f32", tokens=467, seg_lens=(17, 64, 129, 257),
+        seg_starts=(0, 63, 255, 512), scale=0.125,
+        description="causal packed prefill of four requests with histories, GQA 12/3, f32"),
     # The 14B decode shape at a serving batch of 128: 1.7 GB of K/V per layer, several times
     # the last-level cache, so the step streams from HBM.  A throughput shape beside the
     # batch-1 one (same recipe; one split per sequence fills the device).
@@ -368,8 +390,10 @@ def make_prefill_case(rng: np.random.Generator, *, hq, hkv, head_dim, page_size,
 def workload_prefill_case(w: Workload, poison=True) -> PrefillCase:
     assert w.kind == "prefill"
     rng = named_rng(w.index)
+    lens = list(w.seg_lens) if w.seg_lens else [w.tokens]
+    starts = list(w.seg_starts) if w.seg_starts else None
     return make_prefill_case(rng, hq=w.hq, hkv=w.hkv, head_dim=w.head_dim,
-                             page_size=w.page_size, dtype=w.dtype, lens=[w.tokens],
+                             page_size=w.page_size, dtype=w.dtype, lens=lens, starts=starts,
                              num_pages=w.num_pages, scale=w.attn_scale, poison=poison)
 
 

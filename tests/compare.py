@@ -28,6 +28,18 @@ def tolerance(dtype: str):
     return (F32_ATOL, F32_RTOL) if dtype == "f32" else (HALF_ATOL, HALF_RTOL)
 
 
+# A second, tighter bar beside the gate above for f16/bf16 K/V on standard-normal data.  The
+# path computes in f32 over exactly widened K/V (the query and the softmax weights carried as
+# two 16-bit terms, residual below 2^-16 of the value), so its error stays near f32 rounding,
+# ~1e-5 here; one dropped position of a 3254-position context moves an output by ~3e-4, and
+# one 16-bit rounding of the query or the weights by ~1e-3, both caught by 1e-4.
+HALF_SECOND_ATOL = 1e-4
+
+
+def second_bar(dtype: str):
+    return (F32_ATOL, 0.0) if dtype == "f32" else (HALF_SECOND_ATOL, 0.0)
+
+
 @dataclass
 class Report:
     n: int

@@ -190,3 +190,37 @@ def test_empty_sequences_in_a_batch(dtype, hq, hkv, d, S):
     assert_bitwise(got, out, "single-launch step vs three launches")
     assert int(fused.counters.abs().sum().item()) == 0, "counters must be left at zero"
     assert_bitwise(host(fused.kp), host(run.kp), "pool after the single-launch write")
+
+
+def test_fused_step_skips_an_invalid_current_token():
+    """The single-launch step stores the current token, and reads it from k_new / v_new, only
+    where kv_page_write would store it: a current token whose page id is out of range (batch
+    row 0) or whose length is past the table's capacity (row 1) is neither stored nor read
+    from k_new / v_new.  Outputs and both pools then equal those of the three-launch step
+    bit for bit, and the invalid rows' pool bytes are left as they were."""
+    announce("single-launch step with an invalid current-token page id and length")
+    rng = wl.rng_for(611)
+    ctx = [100, 64, 37]
+    case = wl.make_decode_case(rng, batch=3, hq=16, hkv=2, head_dim=128, page_size=16,
+                               dtype="bf16", ctx=ctx, num_splits=4, poison=False)
+    P = case.k_pages.shape[0]
+    cap = case.page_table.shape[1] * 16
+    case.page_table[0, (ctx[0] - 1) // 16] = P               # out-of-range page id
+    case.context_lens[1] = cap + 5                            # past the table's capacity
+    case.token_position[:] = case.context_lens - 1
+    three = DecodeRun(case)
+    out3 = three.step()
+    one = DecodeRun(case)
+    out1 = one.fused_step()
+    assert_bitwise(out1, out3, "single launch vs three launches")
+    assert_bitwise(host(one.kp), host(three.kp), "K pool: single launch vs three launches")
+    assert_bitwise(host(one.vp), host(three.vp), "V pool: single launch vs three launches")
+    # Only row 2's current slot changed.
+    p2 = case.page_table[2, (ctx[2] - 1) // 16]
+    for name, pool, before, new in (("K", one.kp, case.k_pages, case.k_new),
+                                    ("V", one.vp, case.v_pages, case.v_new)):
+        after = host(pool)
+        expect = before.copy()
+        expect[p2, (ctx[2] - 1) % 16] = new[2]
+        assert_bitwise(after, expect, f"{name} pool: only the valid row's slot is written")
+    assert int(one.counters.abs().sum().item()) == 0, "counters must be left at zero"

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import paged_gqa_attention_decode_amd as pa
-from compare import assert_bitwise, assert_within, tolerance
+from compare import assert_bitwise, assert_within, second_bar, tolerance
 from gpu_helpers import DEV, DecodeRun, announce, dev, host
 from paged_gqa_attention_decode_amd import workloads as wl
 
@@ -68,6 +68,7 @@ def test_random_decode(i):
     ref = oracle.decode(case.q[live], kp, vp, case.dtype, case.page_table[live],
                         case.context_lens[live], case.scale, window=c["window"])
     assert_within(out[live], ref, *tolerance(case.dtype), f"random decode {i}")
+    assert_within(out[live], ref, *second_bar(case.dtype), f"random decode {i}, second bar")
     empty = [b for b, n in enumerate(c["ctx"]) if n == 0]
     assert np.all(out[empty] == 0.0), "empty sequences give zero rows"
     fused = DecodeRun(case).fused_step()
@@ -98,3 +99,22 @@ def test_random_prefill(i):
     covered = case.token_table_index >= 0
     assert np.all(got[~covered] == 7.0), "rows outside every segment stay untouched"
     assert_within(got[covered], ref[covered], *tolerance(case.dtype), f"random prefill {i}")
+
+
+@pytest.mark.parametrize("g,hkv,d", [(9, 1, 128), (25, 1, 128), (19, 2, 64), (33, 1, 128),
+                                     (60, 1, 64), (9, 1, 256)])
+def test_decode_group_sizes_split_over_head_groups(g, hkv, d):
+    """Group sizes whose query heads the host spreads over several workgroups when the grid
+    would leave compute units idle (batch 1, few splits): every head is computed once and
+    matches the oracle, and the single-launch step gives the same bits."""
+    announce(f"decode group size {g} hkv={hkv} d={d}")
+    rng = wl.rng_for([904, g, hkv, d])
+    case = wl.make_decode_case(rng, batch=1, hq=g * hkv, hkv=hkv, head_dim=d, page_size=16,
+                               dtype="bf16", ctx=[421], num_splits=3)
+    out = DecodeRun(case).step()
+    kp, vp = oracle.kv_write(case.k_new, case.v_new, case.k_pages, case.v_pages, case.dtype,
+                             case.page_table, case.token_table_index, case.token_position)
+    ref = oracle.decode(case.q, kp, vp, case.dtype, case.page_table, case.context_lens,
+                        case.scale)
+    assert_within(out, ref, *tolerance(case.dtype), f"group {g}")
+    assert_bitwise(DecodeRun(case).fused_step(), out, f"group {g}: single launch vs three")

@@ -68,3 +68,33 @@ def test_prefill_case_layout():
     live = ~np.isnan(c.k_pages.view(np.float16)[:, :, 0, 0])
     assert live.sum() == 30
     assert live[t1[0]].all() and live[t1[1], :14].all() and not live[t1[1], 14:].any()
+
+
+def test_prefill_benchmark_packs_match_the_printed_extents():
+    """The three prefill measurement packs are the pages' shapes: their sums of causal
+    positions equal the values the crucible results page prints (tests/golden)."""
+    printed = {}
+    with open(__file__.replace("test_workloads.py", "golden/causal_positions.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            name, _, _, total = [x.strip() for x in line.split("|")]
+            printed[name] = int(total)
+    for wname, shape in (("prefill_hq12_hkv3_d64_t512_f32", "single-512"),
+                         ("prefill_hq12_hkv3_d64_4x256_f32", "4x256"),
+                         ("prefill_hq12_hkv3_d64_hetero_f32", "heterogeneous")):
+        c = wl.workload_prefill_case(wl.WORKLOADS[wname], poison=False)
+        total = sum(int(a0) * int(n) + int(n) * (int(n) + 1) // 2
+                    for _, n, a0, _ in c.seg_desc.tolist())
+        assert total == printed[shape], (wname, total, printed[shape])
+        assert c.q.shape[0] == c.seg_desc[:, 1].sum()
+
+
+def test_c4_rotations_exceed_the_last_level_cache():
+    w = wl.WORKLOADS["decode_hq28_hkv4_d128_ctx1641_f16"]
+    c = wl.workload_decode_case(w, poison=False)
+    assert len(c.extra_tables) + 1 == 4
+    used = [set(t[t >= 0].tolist()) for t in [c.page_table] + c.extra_tables]
+    assert all(not (used[i] & used[j]) for i in range(4) for j in range(i + 1, 4))
+    per_layer = 4 * 103 * 16 * 4 * 128 * 2 * 2       # 4 page sets, K and V, f16
+    assert w.layers * per_layer > 256 * 2**20
