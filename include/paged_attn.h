@@ -8,6 +8,7 @@
  *   paged_attn_decode        one query row per sequence, split-KV partial softmax
  *   paged_attn_combine       log-sum-exp merge of the split partials
  *   paged_attn_decode_fused  the three above for one decode step, in a single launch
+ *   paged_attn_decode_fused_noalloc  the same step with a library-owned workspace
  *   paged_attn_prefill       causal attention for packed prompt segments
  *
  * Sources (the method these calls implement):
@@ -29,7 +30,9 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library allocates
  *     nothing, keeps no data between calls and is re-entrant (paged_attn_decode_fused keeps
- *     its per-call state in the caller's counter buffer; see there).
+ *     its per-call state in the caller's counter buffer; see there).  The one exception is
+ *     paged_attn_decode_fused_noalloc, whose workspace is a fixed library-owned array per GPU
+ *     shared by its calls (see there).
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null stream).
  *     No call synchronises; ordering is stream order, so a kv_page_write enqueued before an
  *     attention call on the same stream is visible to it.
@@ -78,7 +81,9 @@ typedef enum pa_status {
     PA_EINVAL = -1,        /* malformed argument: null pointer, bad shape, overflow          */
     PA_EUNSUPPORTED = -2,  /* well-formed but not built: head_dim, dtype, group size          */
     PA_ELAUNCH = -3,       /* the HIP runtime rejected a launch (no device, bad stream, ...)  */
-    PA_EDATA = -4          /* checked build only: device metadata out of range (see below)    */
+    PA_EDATA = -4,         /* checked build only: device metadata out of range (see below)    */
+    PA_ESCRATCH = -5       /* paged_attn_decode_fused_noalloc: the call's split workspace does
+                              not fit the library's fixed no-allocation workspace              */
 } pa_status;
 
 /* Short English text for a status code (static storage, never NULL). */
@@ -165,6 +170,35 @@ int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new
 /* Number of uint32 counters paged_attn_decode_fused needs at any head_dim, or 0 for invalid
  * arguments: num_seqs * num_kv_heads * 2 * ceil((Hq/Hkv) / 8). */
 size_t paged_attn_decode_fused_counters(int num_seqs, int num_q_heads, int num_kv_heads);
+
+/*
+ * paged_attn_decode_fused for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The same step on the
+ * same arguments, minus the caller's split workspace and counters, with the same result bit
+ * for bit.  The partials and counters live in one library-owned device array per GPU of
+ * paged_attn_noalloc_scratch_bytes() bytes (16 MiB), placed in that GPU's memory when the
+ * library is first used on it and held until the process ends; the call itself allocates
+ * nothing and frees nothing.
+ *   Limits: the split workspace (paged_attn_decode_workspace_bytes(num_seqs, num_q_heads,
+ *   head_dim, num_splits), e.g. 8.5 MB for 16 sequences x 64 heads x 16 splits at head_dim
+ *   128) must fit in 16 MiB - 64 KiB, and the counters (paged_attn_decode_fused_counters)
+ *   in 64 KiB (16384 of them); a larger call returns PA_ESCRATCH and enqueues nothing.
+ *   Sharing: every call on one GPU uses that GPU's array, which keeps the last call's partials.
+ *   Calls that overlap in time on one GPU (different streams or host threads) race and give
+ *   undefined results: enqueue them on one stream.  The counters start at zero and every call
+ *   leaves them at zero, so no clearing is needed between calls.
+ * Arguments, rules and other errors as for paged_attn_decode_fused.
+ */
+int paged_attn_decode_fused_noalloc(const float* q, const void* k_new, const void* v_new,
+                                    void* k_pages, void* v_pages, pa_dtype kv_dtype,
+                                    const int32_t* page_table, const int32_t* context_lens,
+                                    int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int page_size, int num_pages,
+                                    int max_pages_per_seq, float scale, int window,
+                                    int num_splits, float* out, void* stream);
+
+/* Bytes of the fixed per-GPU workspace of paged_attn_decode_fused_noalloc. */
+size_t paged_attn_noalloc_scratch_bytes(void);
 
 /*
  * Merge of split partials ([crucible-readme] "Split-position attention": rescale each chunk

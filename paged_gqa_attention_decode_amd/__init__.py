@@ -20,13 +20,14 @@ LIB_PATH = os.path.join(_HERE, "libpaged_attn.so")
 # PAGED_ATTN_CHECKED=1 in the environment.
 CHECKED_LIB_PATH = os.path.join(_HERE, "libpaged_attn_checked.so")
 
-PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_ELAUNCH, PA_EDATA = 0, -1, -2, -3, -4
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_ELAUNCH, PA_EDATA, PA_ESCRATCH = 0, -1, -2, -3, -4, -5
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_ROPE_ADJACENT, PA_ROPE_HALVES = 0, 1
 
 C_FUNCTIONS = ("paged_attn_status_string", "paged_attn_decode_workspace_bytes",
                "paged_attn_decode", "paged_attn_decode_fused",
-               "paged_attn_decode_fused_counters", "paged_attn_combine", "paged_attn_prefill",
+               "paged_attn_decode_fused_counters", "paged_attn_decode_fused_noalloc",
+               "paged_attn_noalloc_scratch_bytes", "paged_attn_combine", "paged_attn_prefill",
                "kv_page_write", "kv_page_write_rope")
 
 
@@ -65,6 +66,10 @@ def raw_library(checked: bool | None = None):
                                           p]
         lib.paged_attn_decode_fused.argtypes = [p, p, p, p, p, i, p, p, i, i, i, i, i, i, i, f,
                                                 i, i, p, p, p, p, p]
+        lib.paged_attn_decode_fused_noalloc.argtypes = [p, p, p, p, p, i, p, p, i, i, i, i, i,
+                                                        i, i, f, i, i, p, p]
+        lib.paged_attn_noalloc_scratch_bytes.argtypes = []
+        lib.paged_attn_noalloc_scratch_bytes.restype = ctypes.c_size_t
         lib.paged_attn_decode_fused_counters.argtypes = [i, i, i]
         lib.paged_attn_decode_fused_counters.restype = ctypes.c_size_t
         lib.paged_attn_combine.argtypes = [p, p, i, i, i, i, p, p]
@@ -73,7 +78,8 @@ def raw_library(checked: bool | None = None):
         lib.kv_page_write.argtypes = [p, p, p, p, i, p, p, p, i, i, i, i, i, i, i, p]
         lib.kv_page_write_rope.argtypes = [p, p, p, p, i, p, p, p, p, i, p, i, i, i, i, i, i,
                                            i, i, p]
-        for name in ("paged_attn_decode", "paged_attn_decode_fused", "paged_attn_combine",
+        for name in ("paged_attn_decode", "paged_attn_decode_fused",
+                     "paged_attn_decode_fused_noalloc", "paged_attn_combine",
                      "paged_attn_prefill", "kv_page_write", "kv_page_write_rope"):
             getattr(lib, name).restype = ctypes.c_int
         _libs[path] = lib
@@ -208,6 +214,38 @@ def paged_attn_decode_fused(q, k_new, v_new, k_pages, v_pages, page_table, conte
         _dev(partial_ml, "partial_ml", torch.float32), _dev(counters, "counters"),
         _dev(out, "out", torch.float32, 3), _stream_handle(stream))
     _ok("paged_attn_decode_fused", rc)
+
+
+def paged_attn_noalloc_scratch_bytes() -> int:
+    return int(raw_library().paged_attn_noalloc_scratch_bytes())
+
+
+def paged_attn_decode_fused_noalloc(q, k_new, v_new, k_pages, v_pages, page_table,
+                                    context_lens, scale: float, num_splits: int, out,
+                                    stream=None, window: int = 0) -> None:
+    """paged_attn_decode_fused with the split partials and counters in the library's fixed
+    per-GPU workspace instead of caller buffers (for callers that cannot allocate, e.g.
+    under graph capture).  Raises PagedAttnError with PA_ESCRATCH when the call's split
+    workspace does not fit; calls on one GPU must not overlap in time."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    P, ps, Hkv, Dk = k_pages.shape
+    if Dk != D or tuple(v_pages.shape) != tuple(k_pages.shape) or v_pages.dtype != k_pages.dtype:
+        raise ValueError("k_pages / v_pages shapes or dtypes disagree with q")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (B, Hkv, D) or t.dtype != k_pages.dtype:
+            raise ValueError(f"{name} must be [B, Hkv, D] in the cache dtype")
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B,Hq,D]")
+    rc = raw_library().paged_attn_decode_fused_noalloc(
+        _dev(q, "q", torch.float32, 3), _dev(k_new, "k_new", ndim=3),
+        _dev(v_new, "v_new", ndim=3), _dev(k_pages, "k_pages", ndim=4),
+        _dev(v_pages, "v_pages", ndim=4), _kv_dtype(k_pages),
+        _dev(page_table, "page_table", torch.int32, 2),
+        _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D, ps, P,
+        page_table.shape[1], float(scale), int(window), int(num_splits),
+        _dev(out, "out", torch.float32, 3), _stream_handle(stream))
+    _ok("paged_attn_decode_fused_noalloc", rc)
 
 
 def paged_attn_combine(partial_o, partial_ml, out, stream=None) -> None:

@@ -24,7 +24,7 @@ LIB_CHECKED = os.path.join(HERE, "libpaged_attn_checked.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["api.hip", "decode.hip", "combine.hip", "prefill.hip", "kv_write.hip",
-           "kv_write_rope.hip"]
+           "kv_write_rope.hip", "noalloc.hip"]
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

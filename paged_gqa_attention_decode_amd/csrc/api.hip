@@ -104,6 +104,7 @@ const char* paged_attn_status_string(int status) {
         case PA_EUNSUPPORTED: return "unsupported configuration";
         case PA_ELAUNCH: return "kernel launch failed";
         case PA_EDATA: return "device metadata out of range (checked build)";
+        case PA_ESCRATCH: return "larger than the fixed no-allocation workspace";
         default: return "unknown status";
     }
 }
@@ -236,6 +237,48 @@ int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new
     a.out = out;
     return launched(pa::launch_decode(a, kv_dtype, head_dim, true, (hipStream_t)stream),
                     stream);
+}
+
+size_t paged_attn_noalloc_scratch_bytes(void) { return pa::kNoallocScratchBytes; }
+
+int paged_attn_decode_fused_noalloc(const float* q, const void* k_new, const void* v_new,
+                                    void* k_pages, void* v_pages, pa_dtype kv_dtype,
+                                    const int32_t* page_table, const int32_t* context_lens,
+                                    int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int page_size, int num_pages,
+                                    int max_pages_per_seq, float scale, int window,
+                                    int num_splits, float* out, void* stream) {
+    if (num_seqs < 0) return PA_EINVAL;
+    if (num_seqs == 0) return PA_OK;
+    if (!k_new || !v_new || !out) return PA_EINVAL;
+    if (num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || num_splits < 1 ||
+        num_q_heads % num_kv_heads != 0)
+        return PA_EINVAL;
+    // Workspace layout inside the fixed array: the counters in a region of their own at the
+    // start (zero when the library is loaded, and every call leaves them zero, whatever the
+    // sizes of earlier calls), then partial_o and partial_ml, each at a 256-byte boundary.
+    // Sizes are checked before anything touches the device.
+    const size_t po_bytes =
+        paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_splits);
+    const size_t n_counters = paged_attn_decode_fused_counters(num_seqs, num_q_heads,
+                                                               num_kv_heads);
+    if (po_bytes == 0 || n_counters == 0) return PA_EINVAL;
+    if (n_counters * sizeof(uint32_t) > pa::kNoallocCounterBytes) return PA_ESCRATCH;
+    const size_t o_bytes = po_bytes / (size_t)(head_dim + 2) * (size_t)head_dim;
+    const size_t ml_bytes = po_bytes - o_bytes;
+    auto up256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t o_off = pa::kNoallocCounterBytes;
+    const size_t ml_off = up256(o_off + o_bytes);
+    if (ml_off + ml_bytes > pa::kNoallocScratchBytes) return PA_ESCRATCH;
+    void* base = nullptr;
+    if (pa::noalloc_scratch(&base) != hipSuccess) return PA_ELAUNCH;
+    char* ws = static_cast<char*>(base);
+    return paged_attn_decode_fused(q, k_new, v_new, k_pages, v_pages, kv_dtype, page_table,
+                                   context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   page_size, num_pages, max_pages_per_seq, scale, window,
+                                   num_splits, reinterpret_cast<float*>(ws + o_off),
+                                   reinterpret_cast<float*>(ws + ml_off),
+                                   reinterpret_cast<uint32_t*>(ws), out, stream);
 }
 
 int paged_attn_combine(const float* partial_o, const float* partial_ml, int num_seqs,

@@ -287,6 +287,13 @@ hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 hipError_t launch_kv_write_rope(const KvRopeArgs& a, int kv_dtype, hipStream_t stream);
 
+// The no-allocation decode step's workspace: one fixed device array per GPU (noalloc.hip)
+// of kNoallocScratchBytes bytes.  *ptr receives its device address on the current device
+// (looked up once per device).
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+constexpr size_t kNoallocCounterBytes = size_t(64) << 10;  // at its start: counters only
+hipError_t noalloc_scratch(void** ptr);
+
 // Checked build: read and clear each kernel file's metadata flag (synchronous copies; call
 // after the stream has been synchronised).  *bad is set when the flag was marked.
 hipError_t take_bad_metadata_decode(int* bad);

@@ -53,6 +53,7 @@ def test_status_strings():
     assert pa.paged_attn_status_string(-2) == "unsupported configuration"
     assert pa.paged_attn_status_string(-3) == "kernel launch failed"
     assert pa.paged_attn_status_string(-4) == "device metadata out of range (checked build)"
+    assert pa.paged_attn_status_string(-5) == "larger than the fixed no-allocation workspace"
     assert pa.paged_attn_status_string(42) == "unknown status"
 
 
@@ -240,3 +241,26 @@ def test_python_binding_rejects_host_tensors():
         pa.paged_attn_decode(q, k, k, torch.zeros(1, 16, dtype=torch.int32),
                              torch.ones(1, dtype=torch.int32), 0.125,
                              torch.zeros(1, 8, 4, 64), torch.zeros(1, 8, 4, 2))
+
+
+# decode_fused_noalloc(q, k_new, v_new, k, v, dtype, table, ctx, B, Hq, Hkv, D, ps, P, maxp,
+#                      scale, window, S, out, stream)
+def noalloc(**kw):
+    a = dict(GOOD_DECODE, **kw)
+    return pa.raw_library().paged_attn_decode_fused_noalloc(
+        a["q"], FAKE, FAKE, a["k"], a["v"], a["dtype"], a["table"], a["ctx"], a["B"], a["Hq"],
+        a["Hkv"], a["D"], a["ps"], a["P"], a["maxp"], a["scale"], a["window"], a["S"], FAKE, NULL)
+
+
+def test_noalloc_workspace_limits_are_checked_before_the_device():
+    """The no-allocation step rejects a call whose partials or counters do not fit its fixed
+    array with PA_ESCRATCH, and malformed arguments with PA_EINVAL, before any device call."""
+    assert pa.paged_attn_noalloc_scratch_bytes() == 16 << 20
+    assert noalloc(S=0) == pa.PA_EINVAL
+    assert noalloc(Hq=41) == pa.PA_EINVAL
+    assert noalloc(B=-1) == pa.PA_EINVAL
+    # 64 sequences x 64 heads x 512 splits x 130 floats = 1.09 GB of partials
+    assert noalloc(B=64, Hq=64, Hkv=8, S=512) == pa.PA_ESCRATCH
+    # 20000 sequences x 8 KV heads x 2 counters = 320,000 counters > 16,384
+    assert noalloc(B=20000, Hq=8, Hkv=8, S=1, D=64) == pa.PA_ESCRATCH
+    assert noalloc(B=0) == pa.PA_OK

@@ -1,0 +1,77 @@
+"""GPU: paged_attn_decode_fused_noalloc, the single-launch decode step whose split workspace is
+the library's fixed per-GPU array, against paged_attn_decode_fused with caller buffers.
+
+Two calls in a row on one GPU, the second with a smaller problem than the first (so the
+array holds the first call's partials and a different counter layout when the second one
+runs): each must give paged_attn_decode_fused's output and pools bit for bit, and the second
+also matches the oracle within the 16-bit tolerance.  A call whose workspace exceeds the
+array is rejected with PA_ESCRATCH before anything is enqueued."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_gqa_attention_decode_amd as pa
+from compare import assert_bitwise, assert_within, tolerance
+from gpu_helpers import DEV, DecodeRun, announce, host
+from paged_gqa_attention_decode_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def _noalloc_step(case):
+    run = DecodeRun(case)
+    B, Hq, D = case.q.shape
+    out = torch.full((B, Hq, D), float("nan"), device=DEV)
+    pa.paged_attn_decode_fused_noalloc(run.q, run.k_new, run.v_new, run.kp, run.vp, run.table,
+                                       run.ctx, case.scale, run.S, out, window=run.window)
+    torch.cuda.synchronize()
+    return host(out), host(run.kp), host(run.vp)
+
+
+def _fused_step(case):
+    run = DecodeRun(case)
+    out = run.fused_step()
+    return out, host(run.kp), host(run.vp)
+
+
+def test_noalloc_step_equals_fused_step_on_two_calls():
+    first = wl.make_decode_case(wl.rng_for(950), batch=16, hq=64, hkv=8, head_dim=128,
+                                page_size=32, dtype="bf16", ctx_range=(64, 4096),
+                                num_pages=2048, num_splits=16)
+    second = wl.make_decode_case(wl.rng_for(951), batch=3, hq=40, hkv=8, head_dim=128,
+                                 page_size=16, dtype="f16", ctx=[3254, 17, 900], num_splits=32)
+    sizes = [pa.paged_attn_decode_workspace_bytes(c.q.shape[0], c.q.shape[1], c.q.shape[2],
+                                                  c.num_splits) for c in (first, second)]
+    assert sizes[1] < sizes[0] <= pa.paged_attn_noalloc_scratch_bytes()
+    for name, case in (("first (batch 16, 16 splits)", first), ("second (batch 3)", second)):
+        announce(f"no-alloc decode step, {name}")
+        got, gk, gv = _noalloc_step(case)
+        ref, rk, rv = _fused_step(case)
+        assert_bitwise(got, ref, f"{name}: output")
+        assert_bitwise(gk, rk, f"{name}: K pool")
+        assert_bitwise(gv, rv, f"{name}: V pool")
+    kp, vp = oracle.kv_write(second.k_new, second.v_new, second.k_pages, second.v_pages,
+                             second.dtype, second.page_table, second.token_table_index,
+                             second.token_position)
+    want = oracle.decode(second.q, kp, vp, second.dtype, second.page_table,
+                         second.context_lens, second.scale)
+    assert_within(got, want, *tolerance(second.dtype), "second call vs the oracle")
+
+
+def test_noalloc_step_rejects_a_workspace_larger_than_the_array():
+    announce("no-alloc decode step: oversize rejection")
+    case = wl.make_decode_case(wl.rng_for(952), batch=2, hq=8, hkv=2, head_dim=64,
+                               page_size=16, dtype="f32", ctx=[40, 7], num_splits=2)
+    run = DecodeRun(case)
+    out = torch.zeros(2, 8, 64, device=DEV)
+    # 4096 splits x 2 sequences x 8 heads x 66 floats = 17.3 MB > 16 MiB.
+    with pytest.raises(pa.PagedAttnError) as err:
+        pa.paged_attn_decode_fused_noalloc(run.q, run.k_new, run.v_new, run.kp, run.vp,
+                                           run.table, run.ctx, case.scale, 4096, out)
+    assert err.value.status == pa.PA_ESCRATCH
+    torch.cuda.synchronize()
+    assert np.all(host(out) == 0.0), "a rejected call writes nothing"
