@@ -75,3 +75,37 @@ def test_noalloc_step_rejects_a_workspace_larger_than_the_array():
     assert err.value.status == pa.PA_ESCRATCH
     torch.cuda.synchronize()
     assert np.all(host(out) == 0.0), "a rejected call writes nothing"
+
+
+def test_noalloc_step_in_a_graph():
+    """The use the entry is for: captured once into a HIP graph (no allocation in the call)
+    and replayed three times, with eager work between the replays (another no-allocation
+    call on a different problem, which overwrites the array's partials); every replay equals
+    the eager single-launch step bit for bit."""
+    announce("no-alloc decode step captured in a graph")
+    case = wl.make_decode_case(wl.rng_for(953), batch=4, hq=40, hkv=8, head_dim=128,
+                               page_size=16, dtype="f16", ctx=[3254, 1, 640, 2049],
+                               num_splits=32)
+    other = wl.make_decode_case(wl.rng_for(954), batch=2, hq=64, hkv=8, head_dim=128,
+                                page_size=32, dtype="bf16", ctx=[4000, 77], num_splits=8)
+    eager, _, _ = _fused_step(case)
+    _noalloc_step(other)  # the array's address is looked up here, outside the capture
+
+    run = DecodeRun(case)
+    B, Hq, D = case.q.shape
+    out = torch.full((B, Hq, D), float("nan"), device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pa.paged_attn_decode_fused_noalloc(run.q, run.k_new, run.v_new, run.kp, run.vp,
+                                               run.table, run.ctx, case.scale, run.S, out)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise(host(out), eager, f"replay {i}")
+        _noalloc_step(other)
