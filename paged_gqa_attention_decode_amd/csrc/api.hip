@@ -24,8 +24,11 @@ constexpr int64_t kI32Max = 2147483647;
 constexpr int kMaxGridYZ = 65535;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxGroup = 64;
-// Query heads one decode workgroup serves: the 16 columns of a matrix-core block.
+// Query heads one decode workgroup serves: the 16 columns of a matrix-core block (16-bit
+// pools), or 8 on the vector units (f32 pools, whose heads each hold D accumulators per lane
+// group).
 constexpr int kMaxHeadsPerWg = 16;
+constexpr int kMaxHeadsPerWgF32 = 8;
 // The single-launch step's counter buffer holds 2 * ceil(group / 8) counters per KV head
 // (paged_attn_decode_fused_counters), at least twice the head groups of any grid below.
 constexpr int kCounterHeads = 8;
@@ -144,7 +147,8 @@ int make_decode_args(const float* q, const void* k_pages, const void* v_pages, i
         (int64_t)num_seqs * num_q_heads * num_splits * head_dim > kI32Max * 4LL)
         return PA_EINVAL;
     const int group = num_q_heads / num_kv_heads;
-    int head_groups = (group + kMaxHeadsPerWg - 1) / kMaxHeadsPerWg;
+    const int max_heads = kv_dtype == PA_F32 ? kMaxHeadsPerWgF32 : kMaxHeadsPerWg;
+    int head_groups = (group + max_heads - 1) / max_heads;
     // A grid with fewer workgroups than the device has CUs leaves CUs idle: then the query
     // heads of a KV head are spread over twice the workgroups.  Each reads that KV head's
     // rows; workgroups are dealt to the 8 XCDs in turn, so with a split count that is a

@@ -21,12 +21,13 @@
 //         widening and cross-lane reductions, which made that loop issue-bound; a tile costs
 //         32 MFMAs of 16 cycles on one SIMD instead.)
 //   loads each lane reads its K rows as 16-byte pieces of 16 keys x 32 dims per MFMA and its
-//         V as NC consecutive dims of 8 keys.  With a 16-bit pool the next tile's K and V are
-//         both requested as soon as the scores have used this tile's K (V is double-buffered,
-//         K is not), so a tile costs one memory round trip, overlapped with the softmax and
-//         PV product of the tile before it; an f32 pool (twice the bytes per tile) requests
-//         the next V after the PV product.  Requests past a wave's last tile are clamped onto
-//         the split's last row (cache hits).
+//         V as NC consecutive dims of 8 keys.  The next tile's K and V are both requested as
+//         soon as the scores have used this tile's K (V is double-buffered, K is not), so a
+//         tile costs one memory round trip, overlapped with the softmax and PV product of
+//         the tile before it.  Requests past a wave's last tile are clamped onto the split's
+//         last row (cache hits).
+//   pools f16 and bf16 here; f32 pools run on the vector units (decode_valu.h), since the
+//         f32 MFMA has no rate advantage over them and its columns sit mostly idle.
 //   softmax base-2 scores (q pre-scaled by scale * log2 e).  The accumulator is rescaled only
 //         when a head's maximum rises more than kLazyRescale above the reference it was scaled
 //         to; the true maximum is tracked beside it and the partial is normalised to it.
@@ -114,7 +115,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     constexpr int D4 = D / 4;            // float4 columns of an output row
     constexpr int SOH = D + 4;           // floats per (wave, head) accumulator row in LDS
     constexpr int TPT = kTableCap / 64;  // table entries staged per thread (>= 64 threads)
-    constexpr bool kEarlyV = KV::kBytes == 2;  // next tile's V requested with its K
 
     extern __shared__ __align__(16) float lds[];
     __shared__ int s_last;  // single-launch step: this workgroup finished the group's last split
@@ -299,27 +299,21 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         Tile A, B;
         Ops::load_k(A, krow, j0, khi, g, c16);
         Ops::load_v(A, vrow, j0, khi, g, c16);
-        // The next tile's loads: K after this tile's scores; V with it for 16-bit pools, after
-        // the PV product for f32 pools (whose double-buffered V would not fit the registers).
+        // The next tile's K and V, requested once this tile's scores have used its K.
         auto next = [&](Tile& N, int jn) {
             return [&N, jn, &krow, &vrow, khi, g, c16] {
                 Ops::load_k(N, krow, jn, khi, g, c16);
-                if constexpr (kEarlyV) Ops::load_v(N, vrow, jn, khi, g, c16);
-            };
-        };
-        auto next_v = [&](Tile& N, int jn) {
-            return [&N, jn, &vrow, khi, g, c16] {
-                if constexpr (!kEarlyV) Ops::load_v(N, vrow, jn, khi, g, c16);
+                Ops::load_v(N, vrow, jn, khi, g, c16);
             };
         };
         for (;;) {
             int jn = j0 + step;
-            compute_tile(A, j0, r1, next(B, jn), next_v(B, jn));
+            compute_tile(A, j0, r1, next(B, jn), [] {});
             t += nwaves;
             j0 = jn;
             if (t >= ntiles) break;
             jn = j0 + step;
-            compute_tile(B, j0, r1, next(A, jn), next_v(A, jn));
+            compute_tile(B, j0, r1, next(A, jn), [] {});
             t += nwaves;
             j0 = jn;
             if (t >= ntiles) break;
@@ -546,21 +540,29 @@ hipError_t launch_all(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream
         return hipErrorInvalidValue;
     }
     if (head_dim == 64) {
-        if (kv_dtype == 0) return launch_typed<F32, 64, FUSED>(a, stream);
         if (kv_dtype == 1) return launch_typed<F16, 64, FUSED>(a, stream);
-        return launch_typed<BF16, 64, FUSED>(a, stream);
+        if (kv_dtype == 2) return launch_typed<BF16, 64, FUSED>(a, stream);
+        return hipErrorInvalidValue;
     }
-    if (kv_dtype == 0) return launch_typed<F32, 128, FUSED>(a, stream);
     if (kv_dtype == 1) return launch_typed<F16, 128, FUSED>(a, stream);
-    return launch_typed<BF16, 128, FUSED>(a, stream);
+    if (kv_dtype == 2) return launch_typed<BF16, 128, FUSED>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
+}  // namespace pa
+
+#include "decode_valu.h"
+
+namespace pa {
+
 PA_DEFINE_TAKE_BAD_METADATA(take_bad_metadata_decode, g_bad_metadata_decode)
 
+// f32 pools run on the vector units (decode_valu.h), 16-bit pools on the matrix cores.
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, bool fused,
                          hipStream_t stream) {
+    if (kv_dtype == 0) return valu::launch_decode_f32(a, head_dim, fused, stream);
     return fused ? launch_all<true>(a, kv_dtype, head_dim, stream)
                  : launch_all<false>(a, kv_dtype, head_dim, stream);
 }
