@@ -25,10 +25,13 @@ constexpr int kMaxGridYZ = 65535;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxGroup = 64;
 // Query heads one decode workgroup serves: the 16 columns of a matrix-core block (16-bit
-// pools), or 8 on the vector units (f32 pools, whose heads each hold D accumulators per lane
-// group).
+// pools at head_dim 64 and 128), or on the vector units (f32 pools, head_dim 256) 8, and 4 at
+// head_dim 256, where every head holds D accumulators per lane group.
 constexpr int kMaxHeadsPerWg = 16;
-constexpr int kMaxHeadsPerWgF32 = 8;
+int max_heads_per_wg(int kv_dtype, int head_dim) {
+    if (head_dim == 256) return 4;
+    return kv_dtype == PA_F32 ? 8 : kMaxHeadsPerWg;
+}
 // The single-launch step's counter buffer holds 2 * ceil(group / 8) counters per KV head
 // (paged_attn_decode_fused_counters), at least twice the head groups of any grid below.
 constexpr int kCounterHeads = 8;
@@ -147,7 +150,7 @@ int make_decode_args(const float* q, const void* k_pages, const void* v_pages, i
         (int64_t)num_seqs * num_q_heads * num_splits * head_dim > kI32Max * 4LL)
         return PA_EINVAL;
     const int group = num_q_heads / num_kv_heads;
-    const int max_heads = kv_dtype == PA_F32 ? kMaxHeadsPerWgF32 : kMaxHeadsPerWg;
+    const int max_heads = max_heads_per_wg(kv_dtype, head_dim);
     int head_groups = (group + max_heads - 1) / max_heads;
     // A grid with fewer workgroups than the device has CUs leaves CUs idle: then the query
     // heads of a KV head are spread over twice the workgroups.  Each reads that KV head's

@@ -26,8 +26,9 @@
 //         tile costs one memory round trip, overlapped with the softmax and PV product of
 //         the tile before it.  Requests past a wave's last tile are clamped onto the split's
 //         last row (cache hits).
-//   pools f16 and bf16 here; f32 pools run on the vector units (decode_valu.h), since the
-//         f32 MFMA has no rate advantage over them and its columns sit mostly idle.
+//   pools f16 and bf16 at head_dim 64 and 128 here; f32 pools (whose MFMA has no rate
+//         advantage over the vector units) and head_dim 256 run on the vector units
+//         (decode_valu.h).
 //   softmax base-2 scores (q pre-scaled by scale * log2 e).  The accumulator is rescaled only
 //         when a head's maximum rises more than kLazyRescale above the reference it was scaled
 //         to; the true maximum is tracked beside it and the partial is normalised to it.
@@ -66,14 +67,13 @@ constexpr int kCols = 16;        // query heads per workgroup: the columns of an
 // Base-2 headroom of the lazy rescale: probabilities are exp2(s - m_ref) <= 2^8.
 constexpr float kLazyRescale = 8.f;
 
-// Most waves per workgroup: two per SIMD up to head_dim 128, one at 256 (whose q, tile and
-// accumulator registers need more than half a SIMD's register file).
+// Most waves per workgroup (two 4-wave workgroups share a CU at head_dim 128).
 #ifndef PA_DECODE_MAX_WAVES
 #define PA_DECODE_MAX_WAVES 4
 #endif
 template <int D>
 constexpr int max_waves() {
-    return D > 128 ? 4 : PA_DECODE_MAX_WAVES;
+    return PA_DECODE_MAX_WAVES;
 }
 
 __host__ __device__ constexpr int round4(int x) { return (x + 3) & ~3; }
@@ -474,14 +474,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 // Split partials only (paged_attn_decode).
 template <typename KV, int D>
 __global__ void __launch_bounds__(max_waves<D>() * 64)
-    __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2))) decode_split_kernel(DecodeArgs a) {
+    __attribute__((amdgpu_waves_per_eu(2))) decode_split_kernel(DecodeArgs a) {
     decode_body<KV, D, false>(a);
 }
 
 // The single-launch step (paged_attn_decode_fused): page write, partials, last-split merge.
 template <typename KV, int D>
 __global__ void __launch_bounds__(max_waves<D>() * 64)
-    __attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2))) decode_step_kernel(DecodeArgs a) {
+    __attribute__((amdgpu_waves_per_eu(2))) decode_step_kernel(DecodeArgs a) {
     decode_body<KV, D, true>(a);
 }
 
@@ -534,11 +534,6 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
 template <bool FUSED>
 hipError_t launch_all(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
     if (a.heads_per_wg < 1 || a.heads_per_wg > kCols) return hipErrorInvalidValue;
-    if (head_dim == 256) {  // 16-bit K/V only
-        if (kv_dtype == 1) return launch_typed<F16, 256, FUSED>(a, stream);
-        if (kv_dtype == 2) return launch_typed<BF16, 256, FUSED>(a, stream);
-        return hipErrorInvalidValue;
-    }
     if (head_dim == 64) {
         if (kv_dtype == 1) return launch_typed<F16, 64, FUSED>(a, stream);
         if (kv_dtype == 2) return launch_typed<BF16, 64, FUSED>(a, stream);
@@ -559,10 +554,12 @@ namespace pa {
 
 PA_DEFINE_TAKE_BAD_METADATA(take_bad_metadata_decode, g_bad_metadata_decode)
 
-// f32 pools run on the vector units (decode_valu.h), 16-bit pools on the matrix cores.
+// f32 pools and head_dim 256 run on the vector units (decode_valu.h), the other 16-bit
+// pools on the matrix cores.
 hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, bool fused,
                          hipStream_t stream) {
-    if (kv_dtype == 0) return valu::launch_decode_f32(a, head_dim, fused, stream);
+    if (kv_dtype == 0 || head_dim == 256)
+        return valu::launch_decode_valu(a, kv_dtype, head_dim, fused, stream);
     return fused ? launch_all<true>(a, kv_dtype, head_dim, stream)
                  : launch_all<false>(a, kv_dtype, head_dim, stream);
 }

@@ -1,11 +1,13 @@
-// decode_valu.h — the decode kernels for f32 pools, on the vector ALUs (included by
-// decode.hip, in its translation unit).
+// decode_valu.h — the decode kernels on the vector ALUs, for f32 pools and for head_dim 256
+// (included by decode.hip, in its translation unit).
 //
 // Why a second body: the f32 matrix-core instruction (v_mfma_f32_16x16x4_f32) has the same
 // peak rate as the f32 vector units, so it saves issue slots but not time, and its 16-column
 // blocks sit mostly idle at a few query heads per KV head; a 32-key tile of f32 scores is a
-// chain of 32 such MFMAs.  The 16-bit pools, whose MFMA runs at 16 times the vector rate, use
-// the matrix-core body in decode.hip.  Both bodies follow the same method, split rule, lazy
+// chain of 32 such MFMAs.  At head_dim 256 the matrix-core operands of 16 columns need more
+// than half a SIMD's registers, so that body runs one wave per SIMD, and the vector body
+// with at most 4 heads per workgroup measured faster.  The other 16-bit pools use the
+// matrix-core body in decode.hip.  Both bodies follow the same method, split rule, lazy
 // rescale, partial layout and single-launch handoff, and give results within the f32 bar of
 // the oracle; each is deterministic and batch- and grouping-invariant by itself.
 //
@@ -731,23 +733,23 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 // Split partials only (paged_attn_decode).
 template <typename KV, int D, int GH>
 __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
-    __attribute__((amdgpu_waves_per_eu(2))) decode_f32_split_kernel(DecodeArgs a) {
+    __attribute__((amdgpu_waves_per_eu(2))) decode_valu_split_kernel(DecodeArgs a) {
     decode_body<KV, D, GH, false>(a);
 }
 
 // The single-launch step (paged_attn_decode_fused): page write, partials, last-split merge.
 template <typename KV, int D, int GH>
 __global__ void __launch_bounds__((DecodeGeom<KV, D>::kWaves * 64))
-    __attribute__((amdgpu_waves_per_eu(2))) decode_f32_step_kernel(DecodeArgs a) {
+    __attribute__((amdgpu_waves_per_eu(2))) decode_valu_step_kernel(DecodeArgs a) {
     decode_body<KV, D, GH, true>(a);
 }
 
 template <typename KV, int D, int GH, bool FUSED>
 const void* decode_kernel_ptr() {
     if constexpr (FUSED)
-        return (const void*)decode_f32_step_kernel<KV, D, GH>;
+        return (const void*)decode_valu_step_kernel<KV, D, GH>;
     else
-        return (const void*)decode_f32_split_kernel<KV, D, GH>;
+        return (const void*)decode_valu_split_kernel<KV, D, GH>;
 }
 
 template <typename KV, int D, int GH, bool FUSED>
@@ -772,9 +774,9 @@ hipError_t launch_gh(const DecodeArgs& a, int waves, hipStream_t stream) {
     }
     const dim3 grid(a.num_splits, a.num_kv_heads * a.head_groups, a.num_seqs);
     if constexpr (FUSED)
-        hipLaunchKernelGGL((decode_f32_step_kernel<KV, D, GH>), grid, dim3(waves * 64), lds, stream, a);
+        hipLaunchKernelGGL((decode_valu_step_kernel<KV, D, GH>), grid, dim3(waves * 64), lds, stream, a);
     else
-        hipLaunchKernelGGL((decode_f32_split_kernel<KV, D, GH>), grid, dim3(waves * 64), lds, stream,
+        hipLaunchKernelGGL((decode_valu_split_kernel<KV, D, GH>), grid, dim3(waves * 64), lds, stream,
                            a);
     return hipGetLastError();
 }
@@ -813,15 +815,23 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
 }
 
 template <bool FUSED>
-hipError_t launch_all(const DecodeArgs& a, int head_dim, hipStream_t stream) {
-    if (head_dim == 64) return launch_typed<F32, 64, FUSED>(a, stream);
-    if (head_dim == 128) return launch_typed<F32, 128, FUSED>(a, stream);
-    return hipErrorInvalidValue;
+hipError_t launch_all(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
+    if (kv_dtype == 0) {
+        if (head_dim == 64) return launch_typed<F32, 64, FUSED>(a, stream);
+        if (head_dim == 128) return launch_typed<F32, 128, FUSED>(a, stream);
+        return hipErrorInvalidValue;
+    }
+    if (head_dim != 256) return hipErrorInvalidValue;
+    if (kv_dtype == 1) return launch_typed<F16, 256, FUSED>(a, stream);
+    return launch_typed<BF16, 256, FUSED>(a, stream);
 }
 
-// f32 pools: the split kernel or the single-launch step.
-hipError_t launch_decode_f32(const DecodeArgs& a, int head_dim, bool fused, hipStream_t stream) {
-    return fused ? launch_all<true>(a, head_dim, stream) : launch_all<false>(a, head_dim, stream);
+// f32 pools (head_dim 64, 128) and 16-bit pools at head_dim 256: the split kernel or the
+// single-launch step.
+hipError_t launch_decode_valu(const DecodeArgs& a, int kv_dtype, int head_dim, bool fused,
+                              hipStream_t stream) {
+    return fused ? launch_all<true>(a, kv_dtype, head_dim, stream)
+                 : launch_all<false>(a, kv_dtype, head_dim, stream);
 }
 
 }  // namespace valu
