@@ -26,10 +26,14 @@ def checked():
     pa.use_checked_library(False)
 
 
-def _decode_case(ctx=(100, 1000, 37)):
+def _decode_case(ctx=(100, 1000, 37), dtype="f16"):
     rng = wl.rng_for([800, len(ctx)])
     return wl.make_decode_case(rng, batch=len(ctx), hq=8, hkv=2, head_dim=128, page_size=16,
-                               dtype="f16", ctx=list(ctx), num_splits=8)
+                               dtype=dtype, ctx=list(ctx), num_splits=8)
+
+
+# f16 runs the matrix-core decode body, f32 the vector-unit body: both mark the same flags.
+DECODE_DTYPES = pytest.mark.parametrize("dtype", ["f16", "f32"])
 
 
 def _prefill_case():
@@ -56,9 +60,10 @@ def _prefill(c, table=None, desc=None):
     return host(out)
 
 
-def test_valid_calls_match_the_product_library(checked):
-    announce("checked build: valid calls")
-    case = _decode_case()
+@DECODE_DTYPES
+def test_valid_calls_match_the_product_library(checked, dtype):
+    announce(f"checked build: valid calls ({dtype} decode)")
+    case = _decode_case(dtype=dtype)
     a, f = DecodeRun(case).step(), DecodeRun(case).fused_step()
     p = _prefill(_prefill_case())
     pa.use_checked_library(False)
@@ -70,9 +75,10 @@ def test_valid_calls_match_the_product_library(checked):
     assert_bitwise(p, q, "prefill: checked vs product")
 
 
-def test_decode_page_id_out_of_range(checked):
-    announce("checked build: decode with a page id past the pool")
-    case = _decode_case()
+@DECODE_DTYPES
+def test_decode_page_id_out_of_range(checked, dtype):
+    announce(f"checked build: decode with a page id past the pool ({dtype})")
+    case = _decode_case(dtype=dtype)
     case.page_table = case.page_table.copy()
     case.page_table[1, 3] = case.k_pages.shape[0]      # inside sequence 1's 1000 positions
     run = DecodeRun(case)
@@ -80,14 +86,15 @@ def test_decode_page_id_out_of_range(checked):
     _expect_edata(lambda: pa.paged_attn_decode(run.q, run.kp, run.vp, run.table, run.ctx,
                                                case.scale, run.po, run.pml), "decode")
     _expect_edata(lambda: DecodeRun(case).fused_step(), "single-launch step")
-    DecodeRun(_decode_case()).step()                   # clean again
+    DecodeRun(_decode_case(dtype=dtype)).step()        # clean again
     pa.use_checked_library(False)
     DecodeRun(case).step()                             # the product library clamps: OK
 
 
-def test_decode_length_past_capacity(checked):
-    announce("checked build: decode length past the table's capacity")
-    case = _decode_case()
+@DECODE_DTYPES
+def test_decode_length_past_capacity(checked, dtype):
+    announce(f"checked build: decode length past the table's capacity ({dtype})")
+    case = _decode_case(dtype=dtype)
     run = DecodeRun(case)
     run.write()
     cap = case.page_table.shape[1] * case.k_pages.shape[1]
