@@ -1,10 +1,10 @@
 """GPU: paged_attn_decode_fused_noalloc, the single-launch decode step whose split workspace is
 the library's fixed per-GPU array, against paged_attn_decode_fused with caller buffers.
 
-Two calls in a row on one GPU, the second with a smaller problem than the first (so the
-array holds the first call's partials and a different counter layout when the second one
-runs): each must give paged_attn_decode_fused's output and pools bit for bit, and the second
-also matches the oracle within the 16-bit tolerance.  A call whose workspace exceeds the
+Calls in a row on one GPU, each with a smaller problem than the one before (so the array
+holds the previous call's partials and a different counter layout when the next one runs):
+each must give paged_attn_decode_fused's output and pools bit for bit, and the smaller ones
+also match the oracle within their tolerance.  A call whose workspace exceeds the
 array is rejected with PA_ESCRATCH before anything is enqueued."""
 import numpy as np
 import pytest
@@ -44,22 +44,27 @@ def test_noalloc_step_equals_fused_step_on_two_calls():
                                 num_pages=2048, num_splits=16)
     second = wl.make_decode_case(wl.rng_for(951), batch=3, hq=40, hkv=8, head_dim=128,
                                  page_size=16, dtype="f16", ctx=[3254, 17, 900], num_splits=32)
+    # a third, smaller still, on an f32 pool (the vector-unit decode body)
+    third = wl.make_decode_case(wl.rng_for(955), batch=2, hq=8, hkv=2, head_dim=64,
+                                page_size=16, dtype="f32", ctx=[256, 31], num_splits=4)
     sizes = [pa.paged_attn_decode_workspace_bytes(c.q.shape[0], c.q.shape[1], c.q.shape[2],
-                                                  c.num_splits) for c in (first, second)]
-    assert sizes[1] < sizes[0] <= pa.paged_attn_noalloc_scratch_bytes()
-    for name, case in (("first (batch 16, 16 splits)", first), ("second (batch 3)", second)):
+                                                  c.num_splits) for c in (first, second, third)]
+    assert sizes[2] < sizes[1] < sizes[0] <= pa.paged_attn_noalloc_scratch_bytes()
+    for name, case in (("first (batch 16, 16 splits)", first), ("second (batch 3)", second),
+                       ("third (f32, batch 2)", third)):
         announce(f"no-alloc decode step, {name}")
         got, gk, gv = _noalloc_step(case)
         ref, rk, rv = _fused_step(case)
         assert_bitwise(got, ref, f"{name}: output")
         assert_bitwise(gk, rk, f"{name}: K pool")
         assert_bitwise(gv, rv, f"{name}: V pool")
-    kp, vp = oracle.kv_write(second.k_new, second.v_new, second.k_pages, second.v_pages,
-                             second.dtype, second.page_table, second.token_table_index,
-                             second.token_position)
-    want = oracle.decode(second.q, kp, vp, second.dtype, second.page_table,
-                         second.context_lens, second.scale)
-    assert_within(got, want, *tolerance(second.dtype), "second call vs the oracle")
+        if case is not first:
+            kp, vp = oracle.kv_write(case.k_new, case.v_new, case.k_pages, case.v_pages,
+                                     case.dtype, case.page_table, case.token_table_index,
+                                     case.token_position)
+            want = oracle.decode(case.q, kp, vp, case.dtype, case.page_table,
+                                 case.context_lens, case.scale)
+            assert_within(got, want, *tolerance(case.dtype), f"{name} vs the oracle")
 
 
 def test_noalloc_step_rejects_a_workspace_larger_than_the_array():
