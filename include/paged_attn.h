@@ -154,8 +154,9 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
  *                   resets its counter; with num_splits = 1 they are not touched), so the
  *                   buffer is reused without clearing.  One counter per (sequence, KV
  *                   head, head group of the launch): a workgroup serves up to 16 query
- *                   heads, and the launch spreads a KV head's heads over at most
- *                   2 * ceil(G / 16) groups, within the 2 * ceil(G / 8) the buffer holds.
+ *                   heads (8 for f32 pools, 4 at head_dim 256), and the launch spreads a KV
+ *                   head's heads over at most twice that many groups, never more than the
+ *                   2 * ceil(G / 8) the buffer holds.
  *   out             [num_seqs][num_q_heads][head_dim] f32, device, written
  * All other arguments and rules as for paged_attn_decode.  Calls that share a counters
  * buffer must not overlap in time (enqueue them on one stream).
