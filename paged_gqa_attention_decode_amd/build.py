@@ -1,5 +1,6 @@
 """Build libpaged_attn.so, and its checked variant libpaged_attn_checked.so, from csrc/*.hip
-with hipcc for gfx950.
+with hipcc for gfx950; and libpaged_attn_probes.so, the measurement kernels of bench.py
+(csrc/probes.hip), which is not part of the attention library.
 
     python -m paged_gqa_attention_decode_amd.build
 
@@ -21,6 +22,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpaged_attn.so")
 BUILD_CHECKED = os.path.join(HERE, "_build_checked")
 LIB_CHECKED = os.path.join(HERE, "libpaged_attn_checked.so")
+LIB_PROBES = os.path.join(HERE, "libpaged_attn_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["api.hip", "decode.hip", "combine.hip", "prefill.hip", "kv_write.hip",
@@ -58,12 +60,26 @@ def build(verbose: bool = False, extra_flags=(), checked: bool = False) -> str:
     return lib
 
 
+def build_probes(verbose: bool = False) -> str:
+    """libpaged_attn_probes.so from csrc/probes.hip (one translation unit, linked directly)."""
+    tmp = LIB_PROBES + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-shared", os.path.join(CSRC, "probes.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for probes.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB_PROBES)
+    if verbose:
+        print(f"built {LIB_PROBES}")
+    return LIB_PROBES
+
+
 def build_all(verbose: bool = False):
-    """Both libraries, the product and its checked variant, built concurrently."""
-    with cf.ThreadPoolExecutor(2) as ex:
+    """The libraries, the product, its checked variant and the probes, built concurrently."""
+    with cf.ThreadPoolExecutor(3) as ex:
         product = ex.submit(build, verbose)
         checked = ex.submit(build, verbose, (), True)
-        return product.result(), checked.result()
+        probes = ex.submit(build_probes, verbose)
+        return product.result(), checked.result(), probes.result()
 
 
 if __name__ == "__main__":

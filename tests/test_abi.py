@@ -264,3 +264,34 @@ def test_noalloc_workspace_limits_are_checked_before_the_device():
     # 20000 sequences x 8 KV heads x 2 counters = 320,000 counters > 16,384
     assert noalloc(B=20000, Hq=8, Hkv=8, S=1, D=64) == pa.PA_ESCRATCH
     assert noalloc(B=0) == pa.PA_OK
+
+
+def test_probe_library_is_separate_and_rejects_bad_shapes():
+    """The measurement kernels live in their own library: it exports the three probes, the
+    attention library exports none of them, and a shape the walk does not cover is refused
+    on the host (return value hipErrorInvalidValue, nothing launched)."""
+    from paged_gqa_attention_decode_amd import build as hip_build
+    out = subprocess.run(["nm", "-D", "--defined-only", hip_build.LIB_PROBES],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    probes = {"pa_probe_read_walk", "pa_probe_read_plain", "pa_probe_empty"}
+    assert probes <= exported
+    main = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    assert not any(p in main for p in probes)
+    lib = ctypes.CDLL(hip_build.LIB_PROBES)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.pa_probe_read_walk.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, i, i, i, vp, vp]
+    lib.pa_probe_read_plain.argtypes = [vp, vp, ctypes.c_size_t, i, vp, vp]
+    lib.pa_probe_empty.argtypes = [i, vp]
+    invalid = 1  # hipErrorInvalidValue
+    # rows of 24 bytes (head_dim 12 x 2 bytes) are not a whole number of 16-byte pieces
+    assert lib.pa_probe_read_walk(FAKE, FAKE, 2, FAKE, FAKE, 1, 1, 12, 16, 4, 4, 1, 0, FAKE,
+                                  NULL) == invalid
+    # a page size that is not a power of two; a table wider than the staged 4096 entries
+    assert lib.pa_probe_read_walk(FAKE, FAKE, 2, FAKE, FAKE, 1, 1, 128, 24, 4, 4, 1, 0, FAKE,
+                                  NULL) == invalid
+    assert lib.pa_probe_read_walk(FAKE, FAKE, 2, FAKE, FAKE, 1, 1, 128, 16, 4, 4097, 1, 0,
+                                  FAKE, NULL) == invalid
+    assert lib.pa_probe_read_plain(FAKE, FAKE, 24, 4, FAKE, NULL) == invalid
+    assert lib.pa_probe_empty(0, NULL) == invalid
