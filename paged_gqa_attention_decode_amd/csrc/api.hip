@@ -345,6 +345,9 @@ int paged_attn_prefill(const float* q, const void* k_pages, const void* v_pages,
     const int q_blocks = (max_chunk_len + 15) / 16;
     if ((int64_t)q_blocks * num_q_heads > kI32Max) return PA_EUNSUPPORTED;
     a.q_blocks = q_blocks;
+    // One prompt at head_dim 64, two workgroups per CU: the order alternates direction every
+    // CU-count workgroups, so each CU's second workgroup is one of the lightest blocks.
+    a.round_wgs = (num_segs == 1 && head_dim == 64) ? compute_units() : 0;
     return launched(
         pa::launch_prefill(a, kv_dtype, head_dim, q_blocks, (hipStream_t)stream), stream);
 }

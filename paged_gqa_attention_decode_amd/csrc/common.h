@@ -250,6 +250,7 @@ struct PrefillArgs {
     int page_shift, num_pages, max_pages;
     int q_blocks;  // 16-row query blocks of the longest segment
     float qscale;  // scale * log2(e)
+    int round_wgs;  // workgroups dealt per round in alternating order (0: heaviest first only)
 };
 
 struct KvWriteArgs {

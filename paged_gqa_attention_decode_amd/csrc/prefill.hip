@@ -10,7 +10,10 @@
 // gfx950 mapping
 //   grid  (ceil(max_chunk_len / 16) * Hq, 1, num_segs): x enumerates (query block, head)
 //         with the last query blocks (longest causal history) of every head first, so the
-//         heaviest blocks are dispatched before the light ones fill in behind them.  8 waves
+//         heaviest blocks are dispatched before the light ones fill in behind them.  For one
+//         prompt at D = 64 every second round of CU-count workgroups runs in reverse, so that
+//         a CU's two workgroups are a heavy and a light block (they share its matrix cores
+//         and memory pipeline, and a CU holding two heavy blocks set the end).  8 waves
 //         per workgroup, all on the same 16 query rows of one head, held to 128 registers
 //         for D = 64 so that two workgroups share a CU and a whole 512-token prefill is
 //         resident at once (occupancy, not a second register set, hides the load latency).
@@ -100,8 +103,17 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
         ti >= a.num_tables)
         return;
     len = min(min(len, a.total_tokens - start), cap - a0);
-    const int h = (int)(blockIdx.x % (unsigned)a.num_q_heads);
-    const int r0 = (a.q_blocks - 1 - (int)(blockIdx.x / (unsigned)a.num_q_heads)) * kRows;
+    // The workgroup's rank in the heaviest-first order: blockIdx.x itself, or with rounds of
+    // round_wgs workgroups (one per CU) every second round reversed, so that a CU's second
+    // workgroup is one of the lightest blocks and its first one of the heaviest.
+    int rank = (int)blockIdx.x;
+    if (a.round_wgs > 0) {
+        const int rnd = rank / a.round_wgs;
+        const int in_round = min(a.round_wgs, (int)gridDim.x - rnd * a.round_wgs);
+        if (rnd & 1) rank = rnd * a.round_wgs + in_round - 1 - (rank - rnd * a.round_wgs);
+    }
+    const int h = rank % a.num_q_heads;
+    const int r0 = (a.q_blocks - 1 - rank / a.num_q_heads) * kRows;
     if (r0 >= len) return;
 
     const int kvh = h / a.group;
