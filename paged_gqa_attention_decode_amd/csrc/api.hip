@@ -167,6 +167,21 @@ int make_decode_args(const float* q, const void* k_pages, const void* v_pages, i
     // and an empty one): the count follows from the group size.
     head_groups = (group + heads_per_wg - 1) / heads_per_wg;
     if ((int64_t)num_kv_heads * head_groups > kMaxGridYZ) return PA_EUNSUPPORTED;
+    // A batch whose sequences differ in length leaves the CUs that drew the long ones
+    // streaming alone at the end.  On the matrix-core body (16-bit pools, head_dim 64 or 128),
+    // a batch of up to kRankMax sequences whose table rows fit the staged table together, and
+    // whose grid is resident at once (two workgroups per CU), is taken longest first, in
+    // rounds of as many sequences as one workgroup per CU covers, every second round in
+    // reverse: the two workgroups of a CU then hold a long and a short sequence.  The order
+    // changes no bit of any sequence's result.  (A grid of several generations ranks nothing:
+    // there the query, requested after the ranking, costs each workgroup a round trip.)
+    int rank_round = 0;
+    const int64_t per_seq = (int64_t)num_kv_heads * head_groups * num_splits;
+    const int cus = compute_units();
+    if (kv_dtype != PA_F32 && head_dim != 256 && num_seqs > 1 && num_seqs <= pa::kRankMax &&
+        (int64_t)num_seqs * max_pages_per_seq <= pa::kDecodeTableCap && cus > 0 &&
+        per_seq * num_seqs <= 2LL * cus)
+        rank_round = (int)std::max<int64_t>(1, cus / per_seq);
 
     pa::DecodeArgs a = {};
     a.q = q;
@@ -188,6 +203,7 @@ int make_decode_args(const float* q, const void* k_pages, const void* v_pages, i
     a.num_splits = num_splits;
     a.window = window > 0 ? window : 0;
     a.qscale = scale * pa::kLog2e;
+    a.rank_round = rank_round;
     *out = a;
     return PA_OK;
 }

@@ -229,7 +229,14 @@ struct DecodeArgs {
     int page_shift, num_pages, max_pages, num_splits;
     int window;    // sliding window in positions (0: the whole context)
     float qscale;  // scale * log2(e)
+    // > 0: the batch's sequences are taken longest first, in rounds of rank_round sequences
+    // whose direction alternates (0: grid order).  Set only for batches of 2 .. kRankMax
+    // sequences whose table rows fit the staged table together.
+    int rank_round;
 };
+
+constexpr int kRankMax = 64;           // sequences a decode launch can rank (one per lane)
+constexpr int kDecodeTableCap = 2048;  // page-table entries a decode workgroup stages in LDS
 
 struct CombineArgs {
     const float* partial_o;

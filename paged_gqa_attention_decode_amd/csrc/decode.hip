@@ -64,6 +64,13 @@ namespace {
 constexpr int kTableCap = 1024;  // page-table entries staged in LDS at a time
 constexpr int kCols = 16;        // query heads per workgroup: the columns of an MFMA block
 
+// Table entries staged by a workgroup: one sequence's row (or a slice of it), or with a
+// ranked batch every sequence's row.
+template <bool RANKED>
+constexpr int table_cap() {
+    return RANKED ? kDecodeTableCap : kTableCap;
+}
+
 // Base-2 headroom of the lazy rescale: probabilities are exp2(s - m_ref) <= 2^8.
 constexpr float kLazyRescale = 8.f;
 
@@ -78,11 +85,11 @@ constexpr int max_waves() {
 
 __host__ __device__ constexpr int round4(int x) { return (x + 3) & ~3; }
 
-// Dynamic LDS of one workgroup: staged page ids; per (head, wave) the reference maximum, the
+// Dynamic LDS of one workgroup: tcap staged page ids; per (head, wave) the reference maximum, the
 // true maximum and the sum l; per (wave, head) the D accumulators, padded by 16 bytes so the
 // lanes' stores spread over the banks.
-__host__ __device__ constexpr size_t decode_lds_bytes(int waves, int heads, int d) {
-    return (size_t)kTableCap * 4 + (size_t)3 * round4(waves * heads) * 4 +
+__host__ __device__ constexpr size_t decode_lds_bytes(int waves, int heads, int d, int tcap) {
+    return (size_t)tcap * 4 + (size_t)3 * round4(waves * heads) * 4 +
            (size_t)waves * heads * (d + 4) * 4;
 }
 
@@ -106,7 +113,7 @@ struct PartialStore {
     }
 };
 
-template <typename KV, int D, bool FUSED>
+template <typename KV, int D, bool FUSED, bool RANKED>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     using T = typename KV::storage;
     using Ops = TileOps<KV, D>;
@@ -114,6 +121,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     constexpr int NC = D / 16;           // 16-dim blocks of the O^T accumulator
     constexpr int D4 = D / 4;            // float4 columns of an output row
     constexpr int SOH = D + 4;           // floats per (wave, head) accumulator row in LDS
+    constexpr int TCAP = table_cap<RANKED>();
     constexpr int TPT = kTableCap / 64;  // table entries staged per thread (>= 64 threads)
 
     extern __shared__ __align__(16) float lds[];
@@ -123,7 +131,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const int hpw = a.heads_per_wg;
     const int hw = round4(nwaves * hpw);
     int* s_tbl = reinterpret_cast<int*>(lds);
-    float* s_m = lds + kTableCap;  // [head][wave] reference maximum
+    float* s_m = lds + TCAP;       // [head][wave] reference maximum
     float* s_t = s_m + hw;         // [head][wave] true maximum
     float* s_l = s_t + hw;         // [head][wave] sum
     float* s_o = s_l + hw;         // [wave][head][SOH] accumulators
@@ -137,28 +145,63 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const int split = blockIdx.x;
     const int kvh = blockIdx.y / a.head_groups;
     const int hg = blockIdx.y % a.head_groups;
-    const int b = blockIdx.z;
     const int h0 = kvh * a.group + hg * hpw;
     const int nh = min(hpw, a.group - hg * hpw);
+    const int cap = a.max_pages << a.page_shift;
 
     // Nothing here depends on the context length, so the page-table row, the length and the
     // query are requested together, the table first: the K/V loads wait only for the table.
-    const int32_t* trow = a.page_table + (size_t)b * a.max_pages;
-    const bool whole_row = a.max_pages <= kTableCap;
+    // A ranked batch requests every sequence's length and table row (at most kRankMax
+    // sequences, and entries within both the staged table and TPT per thread, which the host
+    // checked), before it knows its own sequence.
+    const int t_count = RANKED ? a.num_seqs * a.max_pages : a.max_pages;
+    const int32_t* tsrc = a.page_table + (RANKED ? (size_t)0 : (size_t)blockIdx.z * a.max_pages);
+    const bool whole_row = t_count <= TCAP && t_count <= TPT * nthreads;
     int tv[TPT];
     if (whole_row) {
 #pragma unroll
         for (int k = 0; k < TPT; ++k) {
             const int i = tid + k * nthreads;
-            tv[k] = (i < a.max_pages) ? trow[i] : 0;
+            tv[k] = (i < t_count) ? tsrc[i] : 0;
         }
     }
-    const int cap = a.max_pages << a.page_shift;
-    const int ctx = clampi(a.context_lens[b], 0, cap);
+    int b = blockIdx.z;
+    int raw_len;
+    if constexpr (RANKED) {
+        // Lane j holds sequence j's length; its rank orders the batch by attended length,
+        // longest first, ties by index.  Grid slot z takes rank z within rounds of rank_round
+        // slots, every second round reversed, so that the workgroups sharing a CU hold a long
+        // and a short sequence.  Every wave computes the same permutation of the batch.
+        const int B = a.num_seqs;
+        const int len_j = (lane < B) ? a.context_lens[lane] : 0;
+        int att = -1;
+        if (lane < B) {
+            att = clampi(len_j, 0, cap);
+            if (a.window > 0) att = min(att, a.window);
+        }
+        int rank = 0;
+        for (int j = 0; j < B; ++j) {
+            const int other = __builtin_amdgcn_readlane(att, j);
+            rank += (other > att || (other == att && j < lane)) ? 1 : 0;
+        }
+        const int z = blockIdx.z;
+        const int R = a.rank_round;
+        const int rnd = z / R;
+        const int in_round = min(R, B - rnd * R);
+        const int want = rnd * R + ((rnd & 1) ? in_round - 1 - (z - rnd * R) : z - rnd * R);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < B && rank == want);
+        b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+        raw_len = __builtin_amdgcn_readlane(len_j, b);
+    } else {
+        raw_len = a.context_lens[b];
+    }
+    const int row_off = RANKED ? b * a.max_pages : 0;  // the sequence's row in the staged table
+    const int32_t* trow = a.page_table + (size_t)b * a.max_pages;
+    const int ctx = clampi(raw_len, 0, cap);
     if constexpr (kChecked) {
         // The length within [0, capacity], and (one workgroup per sequence and KV head) the
         // page ids of the attended positions within [0, num_pages).
-        const int raw = a.context_lens[b];
+        const int raw = raw_len;
         if (raw < 0 || raw > cap) mark_bad(&g_bad_metadata_decode);
         if (split == 0 && hg == 0) {
             const int first = (a.window > 0 && ctx > a.window) ? ctx - a.window : 0;
@@ -177,7 +220,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     // kv_page_write ; paged_attn_decode ; paged_attn_combine for such metadata too.
     int t_new = -1;
     if constexpr (FUSED) {
-        const int raw = a.context_lens[b];
+        const int raw = raw_len;
         if (raw >= 1 && raw <= cap) {
             const int pid = trow[(raw - 1) >> a.page_shift];
             if (pid >= 0 && pid < a.num_pages) t_new = raw - 1;
@@ -192,7 +235,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
         for (int k = 0; k < TPT; ++k) {
             const int i = tid + k * nthreads;
-            if (i < a.max_pages) s_tbl[i] = clampi(tv[k], 0, a.num_pages - 1);
+            if (i < t_count) s_tbl[i] = clampi(tv[k], 0, a.num_pages - 1);
         }
     }
     Ops ops;
@@ -224,7 +267,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const int pmask = (1 << pshift) - 1;
     int pg0 = 0;  // first table entry of the staged slice
     auto pool_row = [&](int key) -> uint64_t {
-        const uint32_t page = (uint32_t)s_tbl[(key >> pshift) - pg0];
+        const uint32_t page = (uint32_t)s_tbl[row_off + (key >> pshift) - pg0];
         return (uint64_t)((page << pshift) | (uint32_t)(key & pmask)) * slot_elems;
     };
     auto krow = [&](int key) -> const T* {
@@ -327,8 +370,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     } else if (lo < hi) {
         const int first = lo >> pshift;
         const int last = (hi - 1) >> pshift;
-        for (int p0 = first; p0 <= last; p0 += kTableCap) {
-            const int n = min(kTableCap, last - p0 + 1);
+        for (int p0 = first; p0 <= last; p0 += TCAP) {
+            const int n = min(TCAP, last - p0 + 1);
             __syncthreads();
             for (int i = tid; i < n; i += nthreads)
                 s_tbl[i] = clampi(trow[p0 + i], 0, a.num_pages - 1);
@@ -344,7 +387,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     if constexpr (FUSED) {
         constexpr int kVec = D * KV::kBytes / 16;
         if (hg == 0 && wave == 0 && lane < kVec && t_new >= lo && t_new < hi) {
-            const uint32_t page = (uint32_t)s_tbl[(t_new >> pshift) - pg0_last];
+            const uint32_t page = (uint32_t)s_tbl[row_off + (t_new >> pshift) - pg0_last];
             const size_t off =
                 (size_t)((page << pshift) | (uint32_t)(t_new & pmask)) * slot_elems +
                 (size_t)kvh * D;
@@ -471,29 +514,29 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     }
 }
 
-// Split partials only (paged_attn_decode).
-template <typename KV, int D>
+// Split partials only (paged_attn_decode).  RANKED: the batch taken longest first.
+template <typename KV, int D, bool RANKED>
 __global__ void __launch_bounds__(max_waves<D>() * 64)
     __attribute__((amdgpu_waves_per_eu(2))) decode_split_kernel(DecodeArgs a) {
-    decode_body<KV, D, false>(a);
+    decode_body<KV, D, false, RANKED>(a);
 }
 
 // The single-launch step (paged_attn_decode_fused): page write, partials, last-split merge.
-template <typename KV, int D>
+template <typename KV, int D, bool RANKED>
 __global__ void __launch_bounds__(max_waves<D>() * 64)
     __attribute__((amdgpu_waves_per_eu(2))) decode_step_kernel(DecodeArgs a) {
-    decode_body<KV, D, true>(a);
+    decode_body<KV, D, true, RANKED>(a);
 }
 
-template <typename KV, int D, bool FUSED>
+template <typename KV, int D, bool FUSED, bool RANKED>
 const void* decode_kernel_ptr() {
     if constexpr (FUSED)
-        return (const void*)decode_step_kernel<KV, D>;
+        return (const void*)decode_step_kernel<KV, D, RANKED>;
     else
-        return (const void*)decode_split_kernel<KV, D>;
+        return (const void*)decode_split_kernel<KV, D, RANKED>;
 }
 
-template <typename KV, int D, bool FUSED>
+template <typename KV, int D, bool FUSED, bool RANKED>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     // Waves per workgroup: enough for one pass of 32-key tiles to cover a split of the
     // table's capacity (lengths live on the device), at most max_waves<D>().  The choice
@@ -505,7 +548,13 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     const int64_t chunk = (cap + a.num_splits - 1) / a.num_splits;
     int waves = (int)std::min<int64_t>(max_waves<D>(), (chunk + kTileKeys - 1) / kTileKeys);
     waves = std::max(waves, 1);
-    const size_t lds = decode_lds_bytes(waves, a.heads_per_wg, D);
+    // A ranked batch stages every table row with kTableCap / 64 entries per thread; with too
+    // few threads for that, the batch runs in grid order (the same results).
+    if constexpr (RANKED) {
+        if ((int64_t)a.num_seqs * a.max_pages > (int64_t)(kTableCap / 64) * waves * 64)
+            return launch_typed<KV, D, FUSED, false>(a, stream);
+    }
+    const size_t lds = decode_lds_bytes(waves, a.heads_per_wg, D, table_cap<RANKED>());
     // Workgroups asking for more than 64 KB of LDS opt in, once per instantiation and device
     // (the largest size granted so far is kept per device; a repeated grant is harmless).
     if (lds > 64 * 1024) {
@@ -514,7 +563,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
         if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
             return hipErrorInvalidDevice;
         if (lds > opted[dev].load(std::memory_order_relaxed)) {
-            hipError_t e = hipFuncSetAttribute(decode_kernel_ptr<KV, D, FUSED>(),
+            hipError_t e = hipFuncSetAttribute(decode_kernel_ptr<KV, D, FUSED, RANKED>(),
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                (int)lds);
             if (e != hipSuccess) return e;
@@ -525,23 +574,38 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     }
     const dim3 grid(a.num_splits, a.num_kv_heads * a.head_groups, a.num_seqs);
     if constexpr (FUSED)
-        hipLaunchKernelGGL((decode_step_kernel<KV, D>), grid, dim3(waves * 64), lds, stream, a);
+        hipLaunchKernelGGL((decode_step_kernel<KV, D, RANKED>), grid, dim3(waves * 64), lds,
+                           stream, a);
     else
-        hipLaunchKernelGGL((decode_split_kernel<KV, D>), grid, dim3(waves * 64), lds, stream, a);
+        hipLaunchKernelGGL((decode_split_kernel<KV, D, RANKED>), grid, dim3(waves * 64), lds,
+                           stream, a);
     return hipGetLastError();
 }
 
-template <bool FUSED>
+template <bool FUSED, bool RANKED>
 hipError_t launch_all(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
-    if (a.heads_per_wg < 1 || a.heads_per_wg > kCols) return hipErrorInvalidValue;
     if (head_dim == 64) {
-        if (kv_dtype == 1) return launch_typed<F16, 64, FUSED>(a, stream);
-        if (kv_dtype == 2) return launch_typed<BF16, 64, FUSED>(a, stream);
+        if (kv_dtype == 1) return launch_typed<F16, 64, FUSED, RANKED>(a, stream);
+        if (kv_dtype == 2) return launch_typed<BF16, 64, FUSED, RANKED>(a, stream);
         return hipErrorInvalidValue;
     }
-    if (kv_dtype == 1) return launch_typed<F16, 128, FUSED>(a, stream);
-    if (kv_dtype == 2) return launch_typed<BF16, 128, FUSED>(a, stream);
+    if (kv_dtype == 1) return launch_typed<F16, 128, FUSED, RANKED>(a, stream);
+    if (kv_dtype == 2) return launch_typed<BF16, 128, FUSED, RANKED>(a, stream);
     return hipErrorInvalidValue;
+}
+
+// A ranked batch (rank_round > 0) runs the instantiation that ranks it; the host sets
+// rank_round only for 2 .. kRankMax sequences whose table rows fit kDecodeTableCap together.
+template <bool FUSED>
+hipError_t launch_mfma(const DecodeArgs& a, int kv_dtype, int head_dim, hipStream_t stream) {
+    if (a.heads_per_wg < 1 || a.heads_per_wg > kCols) return hipErrorInvalidValue;
+    if (a.rank_round > 0) {
+        if (a.num_seqs < 2 || a.num_seqs > kRankMax ||
+            (int64_t)a.num_seqs * a.max_pages > kDecodeTableCap)
+            return hipErrorInvalidValue;
+        return launch_all<FUSED, true>(a, kv_dtype, head_dim, stream);
+    }
+    return launch_all<FUSED, false>(a, kv_dtype, head_dim, stream);
 }
 
 }  // namespace
@@ -560,8 +624,8 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, bool f
                          hipStream_t stream) {
     if (kv_dtype == 0 || head_dim == 256)
         return valu::launch_decode_valu(a, kv_dtype, head_dim, fused, stream);
-    return fused ? launch_all<true>(a, kv_dtype, head_dim, stream)
-                 : launch_all<false>(a, kv_dtype, head_dim, stream);
+    return fused ? launch_mfma<true>(a, kv_dtype, head_dim, stream)
+                 : launch_mfma<false>(a, kv_dtype, head_dim, stream);
 }
 
 }  // namespace pa

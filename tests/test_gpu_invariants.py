@@ -14,7 +14,8 @@ import pytest
 import torch
 
 import paged_gqa_attention_decode_amd as pa
-from compare import assert_bitwise
+import oracle
+from compare import assert_bitwise, assert_within, tolerance
 from gpu_helpers import DEV, DecodeRun, announce, dev, host
 from paged_gqa_attention_decode_amd import workloads as wl
 
@@ -72,11 +73,15 @@ def test_page_permutation_bitwise():
         assert_bitwise(a, b, f"page permutation {name}")
 
 
-def test_batch_composition_bitwise():
-    announce("batch composition bitwise")
+@pytest.mark.parametrize("S", [16, 4])
+def test_batch_composition_bitwise(S):
+    """A sequence's bits do not depend on its batch: alone, batched and in reversed order.
+    At 4 splits the batch's 160 workgroups are resident at once, so the 16-bit decode takes it
+    longest first (ranked in the kernel); at 16 it runs in grid order."""
+    announce(f"batch composition bitwise, {S} splits")
     rng = wl.rng_for(602)
     case = wl.make_decode_case(rng, batch=5, hq=64, hkv=8, head_dim=128, page_size=32,
-                               dtype="bf16", ctx=[4096, 64, 1, 2000, 333], num_splits=16)
+                               dtype="bf16", ctx=[4096, 64, 1, 2000, 333], num_splits=S)
     full = _decode(case)[0]
     for b in range(5):
         sub = wl.DecodeCase(
@@ -224,3 +229,33 @@ def test_fused_step_skips_an_invalid_current_token():
         expect[p2, (ctx[2] - 1) % 16] = new[2]
         assert_bitwise(after, expect, f"{name} pool: only the valid row's slot is written")
     assert int(one.counters.abs().sum().item()) == 0, "counters must be left at zero"
+
+
+def test_ranked_batch_with_ties_and_free_slots():
+    """A batch the 16-bit decode ranks by length (here 12 sequences at 4 splits, resident at
+    once): equal lengths, free slots (length 0) and the longest possible length in one batch.
+    Every sequence equals its own single-sequence call bit for bit, the single-launch step
+    equals the three launches, and the results match the oracle."""
+    announce("ranked batch: ties, free slots")
+    rng = wl.rng_for(607)
+    ctx = [300, 0, 300, 1024, 1, 300, 0, 777, 1024, 2, 300, 64]
+    case = wl.make_decode_case(rng, batch=12, hq=16, hkv=4, head_dim=128, page_size=16,
+                               dtype="f16", ctx=ctx, max_pages_per_seq=64, num_splits=4)
+    run = DecodeRun(case)
+    out = run.step()
+    assert_bitwise(DecodeRun(case).fused_step(), out, "single launch vs three")
+    live = case.context_lens > 0
+    assert np.all(out[~live] == 0.0), "free slots give zero rows"
+    kp, vp = oracle.kv_write(case.k_new, case.v_new, case.k_pages, case.v_pages, case.dtype,
+                             case.page_table, case.token_table_index, case.token_position)
+    ref = oracle.decode(case.q[live], kp, vp, case.dtype, case.page_table[live],
+                        case.context_lens[live], case.scale)
+    assert_within(out[live], ref, *tolerance(case.dtype), "ranked batch vs the oracle")
+    for b in np.flatnonzero(live):
+        sub = wl.DecodeCase(
+            q=case.q[b:b + 1], k_pages=case.k_pages, v_pages=case.v_pages,
+            page_table=case.page_table[b:b + 1], context_lens=case.context_lens[b:b + 1],
+            k_new=case.k_new[b:b + 1], v_new=case.v_new[b:b + 1],
+            token_table_index=np.zeros(1, np.int32), token_position=case.token_position[b:b + 1],
+            dtype=case.dtype, scale=case.scale, num_splits=case.num_splits)
+        assert_bitwise(DecodeRun(sub).step()[0], out[b], f"sequence {b} alone vs ranked batch")
