@@ -142,14 +142,14 @@ WORKLOADS = {
     "decode_b16_hq64_hkv8_d128_ctx64to4096_bf16": Workload(
         name="decode_b16_hq64_hkv8_d128_ctx64to4096_bf16", kind="decode", index=4, hq=64,
         hkv=8, head_dim=128, page_size=32, dtype="bf16", batch=16, ctx_range=(64, 4096),
-        num_pages=8192, num_splits=8, rotations=6,
+        num_pages=8192, num_splits=4, rotations=6,
         description="continuous-batching decode, 16 sequences in a shared 8192-page pool"),
     # Measurement shapes for the windowed and head_dim-256 decode arms (vllm.cpp PR #383
     # names the arms; it fixes no model shape for them): synthetic, same recipe.
     "decode_b16_hq64_hkv8_d128_ctx64to4096_w1024_bf16": Workload(
         name="decode_b16_hq64_hkv8_d128_ctx64to4096_w1024_bf16", kind="decode", index=5,
         hq=64, hkv=8, head_dim=128, page_size=32, dtype="bf16", batch=16, ctx_range=(64, 4096),
-        num_pages=8192, num_splits=8, rotations=6, window=1024,
+        num_pages=8192, num_splits=2, rotations=6, window=1024,
         description="the continuous-batching decode with a 1024-position sliding window"),
     "decode_hq16_hkv8_d256_ctx4096_bf16": Workload(
         name="decode_hq16_hkv8_d256_ctx4096_bf16", kind="decode", index=6, hq=16, hkv=8,
