@@ -5,7 +5,8 @@
 //                        decomposition (one 4-wave workgroup per split, KV head and sequence;
 //                        32-key tiles dealt to the waves in turn; 16-byte lane loads; the
 //                        sequence's page ids staged in LDS; the split rule chunk = ceil(n / S)
-//                        over the attended positions), with no arithmetic and no stores: the
+//                        over the attended positions; with rank_round > 0 the batch taken in
+//                        the decode's ranked order), with no arithmetic and no stores: the
 //                        time of the bytes alone in that order.
 //   pa_probe_read_plain  reads two contiguous regions of the same total size, front to back,
 //                        from enough workgroups to fill the chip.
@@ -31,20 +32,42 @@ template <int P>
 __global__ void __launch_bounds__(kWalkThreads) read_walk(
     const uint4* __restrict__ kp, const uint4* __restrict__ vp, const int32_t* __restrict__ table,
     const int32_t* __restrict__ ctxs, int S, int Hkv, int page_shift, int max_pages,
-    int num_pages, int window, uint32_t* sink) {
+    int num_pages, int window, int rank_round, uint32_t* sink) {
     constexpr int RPI = 64 / P;         // rows per wave instruction
     constexpr int NI = 32 / RPI;        // instructions per 32-key tile, for K and for V
     __shared__ int s_tbl[kWalkTableCap];
     const int split = blockIdx.x;
     const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int cap = max_pages << page_shift;
+    int b = blockIdx.z;
+    if (rank_round > 0) {
+        // The decode's order: sequences ranked by attended length (longest first, ties by
+        // index), slot z taking rank z within rounds of rank_round, every second one reversed.
+        const int B = gridDim.z;
+        int att = -1;
+        if (lane < B) {
+            att = min(max(ctxs[lane], 0), cap);
+            if (window > 0) att = min(att, window);
+        }
+        int rank = 0;
+        for (int j = 0; j < B; ++j) {
+            const int other = __builtin_amdgcn_readlane(att, j);
+            rank += (other > att || (other == att && j < lane)) ? 1 : 0;
+        }
+        const int z = blockIdx.z;
+        const int rnd = z / rank_round;
+        const int in_round = min(rank_round, B - rnd * rank_round);
+        const int want = rnd * rank_round +
+                         ((rnd & 1) ? in_round - 1 - (z - rnd * rank_round) : z - rnd * rank_round);
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < B && rank == want);
+        b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+    }
     const int32_t* trow = table + (size_t)b * max_pages;
     for (int i = tid; i < max_pages; i += kWalkThreads)
         s_tbl[i] = min(max(trow[i], 0), num_pages - 1);
-    const int cap = max_pages << page_shift;
     const int n = min(max(ctxs[b], 0), cap);
     __syncthreads();
     const int w0 = (window > 0 && n > window) ? n - window : 0;
@@ -101,14 +124,16 @@ extern "C" {
 
 // K/V pools [num_pages][page_size][num_kv_heads][head_dim] of elt_bytes-byte elements, a
 // page table [num_seqs][max_pages], lengths [num_seqs], a window (0: none) and a split count,
-// as a decode launch takes them; sink: one writable 32-bit word.  Returns a hipError_t, or
-// hipErrorInvalidValue for a shape the probe does not cover (rows of 128, 256 or 512 bytes,
-// at most 4096 table entries per sequence).
+// as a decode launch takes them; rank_round as the decode sets it for the same call (0: grid
+// order; > 0 needs at most 64 sequences); sink: one writable 32-bit word.  Returns a
+// hipError_t, or hipErrorInvalidValue for a shape the probe does not cover (rows of 128, 256
+// or 512 bytes, at most 4096 table entries per sequence).
 int pa_probe_read_walk(const void* k_pages, const void* v_pages, int elt_bytes,
                        const int32_t* page_table, const int32_t* context_lens, int num_seqs,
                        int num_kv_heads, int head_dim, int page_size, int num_pages,
-                       int max_pages, int num_splits, int window, uint32_t* sink,
-                       void* stream) {
+                       int max_pages, int num_splits, int window, int rank_round,
+                       uint32_t* sink, void* stream) {
+    if (rank_round < 0 || (rank_round > 0 && num_seqs > 64)) return (int)hipErrorInvalidValue;
     if (!k_pages || !v_pages || !page_table || !context_lens || !sink || num_seqs < 1 ||
         num_kv_heads < 1 || num_kv_heads > 65535 || num_seqs > 65535 || num_pages < 1 ||
         max_pages < 1 || max_pages > kWalkTableCap || num_splits < 1 || page_size < 1 ||
@@ -125,15 +150,15 @@ int pa_probe_read_walk(const void* k_pages, const void* v_pages, int elt_bytes,
     if (pieces == 8)
         hipLaunchKernelGGL(read_walk<8>, grid, dim3(kWalkThreads), 0, s, kp, vp, page_table,
                            context_lens, num_splits, num_kv_heads, shift, max_pages, num_pages,
-                           window, sink);
+                           window, rank_round, sink);
     else if (pieces == 16)
         hipLaunchKernelGGL(read_walk<16>, grid, dim3(kWalkThreads), 0, s, kp, vp, page_table,
                            context_lens, num_splits, num_kv_heads, shift, max_pages, num_pages,
-                           window, sink);
+                           window, rank_round, sink);
     else if (pieces == 32)
         hipLaunchKernelGGL(read_walk<32>, grid, dim3(kWalkThreads), 0, s, kp, vp, page_table,
                            context_lens, num_splits, num_kv_heads, shift, max_pages, num_pages,
-                           window, sink);
+                           window, rank_round, sink);
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();

@@ -281,17 +281,20 @@ def test_probe_library_is_separate_and_rejects_bad_shapes():
     assert not any(p in main for p in probes)
     lib = ctypes.CDLL(hip_build.LIB_PROBES)
     vp, i = ctypes.c_void_p, ctypes.c_int
-    lib.pa_probe_read_walk.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, i, i, i, vp, vp]
+    lib.pa_probe_read_walk.argtypes = [vp, vp, i, vp, vp, i, i, i, i, i, i, i, i, i, vp, vp]
     lib.pa_probe_read_plain.argtypes = [vp, vp, ctypes.c_size_t, i, vp, vp]
     lib.pa_probe_empty.argtypes = [i, vp]
     invalid = 1  # hipErrorInvalidValue
     # rows of 24 bytes (head_dim 12 x 2 bytes) are not a whole number of 16-byte pieces
-    assert lib.pa_probe_read_walk(FAKE, FAKE, 2, FAKE, FAKE, 1, 1, 12, 16, 4, 4, 1, 0, FAKE,
-                                  NULL) == invalid
+    assert lib.pa_probe_read_walk(FAKE, FAKE, 2, FAKE, FAKE, 1, 1, 12, 16, 4, 4, 1, 0, 0,
+                                  FAKE, NULL) == invalid
     # a page size that is not a power of two; a table wider than the staged 4096 entries
-    assert lib.pa_probe_read_walk(FAKE, FAKE, 2, FAKE, FAKE, 1, 1, 128, 24, 4, 4, 1, 0, FAKE,
-                                  NULL) == invalid
-    assert lib.pa_probe_read_walk(FAKE, FAKE, 2, FAKE, FAKE, 1, 1, 128, 16, 4, 4097, 1, 0,
+    assert lib.pa_probe_read_walk(FAKE, FAKE, 2, FAKE, FAKE, 1, 1, 128, 24, 4, 4, 1, 0, 0,
+                                  FAKE, NULL) == invalid
+    assert lib.pa_probe_read_walk(FAKE, FAKE, 2, FAKE, FAKE, 1, 1, 128, 16, 4, 4097, 1, 0, 0,
+                                  FAKE, NULL) == invalid
+    # ranking a batch of more than 64 sequences
+    assert lib.pa_probe_read_walk(FAKE, FAKE, 2, FAKE, FAKE, 65, 1, 128, 16, 4, 4, 1, 0, 4,
                                   FAKE, NULL) == invalid
     assert lib.pa_probe_read_plain(FAKE, FAKE, 24, 4, FAKE, NULL) == invalid
     assert lib.pa_probe_empty(0, NULL) == invalid
