@@ -46,6 +46,12 @@
 //   heads the host spreads a KV head's query heads over twice the workgroups when the grid
 //         would leave CUs idle; a head's column computes the same bits whatever the other
 //         columns hold, so every grouping gives the same result.
+//   order a batch of 2 .. kRankMax sequences whose grid is resident at once (at most two
+//         workgroups per CU) runs the RANKED instantiation: every workgroup loads all lengths
+//         and table rows, ranks the batch by attended length, and its grid slot takes the
+//         sequence of that rank, in rounds of CU-count slots whose direction alternates, so
+//         that the two workgroups of a CU hold a long and a short sequence.  A permutation of
+//         the work: every sequence computes the same bits in either order.
 //   window with a sliding window W the splits partition the attended positions
 //         [ctx - W, ctx) (vllm.cpp PR #383 names the windowed arm of the decode kernel).
 //   checks the checked build also marks a length or an attended page id out of range.
