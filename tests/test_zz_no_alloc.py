@@ -2,7 +2,8 @@
 the library's fixed per-GPU array, against paged_attn_decode_fused with caller buffers.
 
 Calls in a row on one GPU, each with a smaller problem than the one before (so the array
-holds the previous call's partials and a different counter layout when the next one runs):
+holds the previous call's partials and a different counter layout when the next one runs),
+over both decode bodies and a batch the matrix-core body ranks:
 each must give paged_attn_decode_fused's output and pools bit for bit, and the smaller ones
 also match the oracle within their tolerance.  A call whose workspace exceeds the
 array is rejected with PA_ESCRATCH before anything is enqueued."""
@@ -47,11 +48,16 @@ def test_noalloc_step_equals_fused_step_on_two_calls():
     # a third, smaller still, on an f32 pool (the vector-unit decode body)
     third = wl.make_decode_case(wl.rng_for(955), batch=2, hq=8, hkv=2, head_dim=64,
                                 page_size=16, dtype="f32", ctx=[256, 31], num_splits=4)
+    # a fourth, the smallest: a bf16 batch whose grid is resident at once, so the matrix-core
+    # body ranks it (longest first)
+    fourth = wl.make_decode_case(wl.rng_for(956), batch=2, hq=8, hkv=2, head_dim=64,
+                                 page_size=16, dtype="bf16", ctx=[45, 300], num_splits=2)
+    cases = (first, second, third, fourth)
     sizes = [pa.paged_attn_decode_workspace_bytes(c.q.shape[0], c.q.shape[1], c.q.shape[2],
-                                                  c.num_splits) for c in (first, second, third)]
-    assert sizes[2] < sizes[1] < sizes[0] <= pa.paged_attn_noalloc_scratch_bytes()
+                                                  c.num_splits) for c in cases]
+    assert sizes[3] < sizes[2] < sizes[1] < sizes[0] <= pa.paged_attn_noalloc_scratch_bytes()
     for name, case in (("first (batch 16, 16 splits)", first), ("second (batch 3)", second),
-                       ("third (f32, batch 2)", third)):
+                       ("third (f32, batch 2)", third), ("fourth (ranked bf16, batch 2)", fourth)):
         announce(f"no-alloc decode step, {name}")
         got, gk, gv = _noalloc_step(case)
         ref, rk, rv = _fused_step(case)
