@@ -39,7 +39,7 @@ def _fused_step(case):
     return out, host(run.kp), host(run.vp)
 
 
-def test_noalloc_step_equals_fused_step_on_two_calls():
+def test_noalloc_step_equals_fused_step_on_calls_in_a_row():
     first = wl.make_decode_case(wl.rng_for(950), batch=16, hq=64, hkv=8, head_dim=128,
                                 page_size=32, dtype="bf16", ctx_range=(64, 4096),
                                 num_pages=2048, num_splits=16)
