@@ -5,9 +5,12 @@
 // carry max = -inf, sum = 0 and get zero weight).
 //
 // gfx950 mapping: D/4 lanes own one (sequence, head) row, one float4 of the output each;
-// a 256-thread workgroup merges 256/(D/4) rows (merge_splits in common.h: the splits are
-// read in chunks of 32 whose loads are all in flight together; a running maximum rescales
-// the accumulators when a later chunk raises it; one division at the end).
+// a 256-thread workgroup merges 256/(D/4) rows (merge_row in common.h: the splits are read
+// in chunks of 32 whose loads are all in flight together; each split's weight is computed
+// once, by the lane that loaded its (m, l), and shared with the row's other lanes through
+// LDS; a running maximum rescales the accumulators when a later chunk raises it; one
+// division at the end).  The partials come from the caller, so an idle split's O may hold
+// anything: its terms are skipped by select.
 #include "common.h"
 
 namespace pa {
@@ -17,14 +20,17 @@ template <int D>
 __global__ void __launch_bounds__(256) combine_kernel(CombineArgs a) {
     constexpr int TPR = D / 4;        // threads per row
     constexpr int RPB = 256 / TPR;    // rows per workgroup
-    const int row = blockIdx.x * RPB + (int)threadIdx.x / TPR;
+    __shared__ float2 s_w[RPB][kMergeChunk];
+    const int rr = (int)threadIdx.x / TPR;
+    const int row = blockIdx.x * RPB + rr;
     const int c = threadIdx.x % TPR;
     if (row >= a.rows) return;
     const int S = a.num_splits;
     const float2* ml = reinterpret_cast<const float2*>(a.partial_ml) + (size_t)row * S;
     const float4* po = reinterpret_cast<const float4*>(a.partial_o) + (size_t)row * S * TPR + c;
     const PlainPartials src{ml, po, TPR};
-    reinterpret_cast<float4*>(a.out)[(size_t)row * TPR + c] = merge_splits(src, S);
+    reinterpret_cast<float4*>(a.out)[(size_t)row * TPR + c] =
+        merge_row<TPR, false>(src, S, c, s_w[rr]);
 }
 
 }  // namespace

@@ -67,6 +67,9 @@ __device__ __forceinline__ float dpp_mov(float v) {
 }
 
 constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i <- lane (i+8) mod 16 (= xor 8)
+constexpr int kDppRor4 = 0x124;        // row_ror:4: lane i <- lane (i+4) mod 16
+constexpr int kDppQuadXor1 = 0xb1;     // quad_perm [1,0,3,2]: lane i <- lane i ^ 1
+constexpr int kDppQuadXor2 = 0x4e;     // quad_perm [2,3,0,1]: lane i <- lane i ^ 2
 
 // Exchanges across 16-lane rows go through the LDS crossbar: ds_swizzle for xor 16 (inside
 // each half-wave) and ds_bpermute for xor 32.  (The gfx950 permlane16/32 row swaps would
@@ -97,6 +100,30 @@ __device__ __forceinline__ float across_groups_max(float v) {
     return v;
 }
 
+// Maximum over each group of N consecutive lanes (N = 16, 32 or 64, groups aligned to N);
+// every lane of a group ends with its group's maximum.  Within a 16-lane row: the quad's
+// two xors, then rotations by 4 and 8 (after the quad steps a lane's quad holds one value,
+// so the rotations cover the other three quads).
+template <int N>
+__device__ __forceinline__ float within_group_max(float v) {
+    v = fmaxf(v, dpp_mov<kDppQuadXor1>(v));
+    v = fmaxf(v, dpp_mov<kDppQuadXor2>(v));
+    v = fmaxf(v, dpp_mov<kDppRor4>(v));
+    v = fmaxf(v, dpp_mov<kDppRor8>(v));
+    if constexpr (N >= 32) v = fmaxf(v, lane_xor16(v));
+    if constexpr (N >= 64) v = fmaxf(v, lane_xor32(v));
+    return v;
+}
+
+// Orders one wave's LDS accesses around it for the compiler: the LDS executes a wave's
+// accesses in issue order, so a lane's read after this sees what other lanes of the same
+// wave wrote before it, and a write after it cannot overtake an earlier read.
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
@@ -124,24 +151,27 @@ struct PlainPartials {
 // with device-scope stores, so each load has to be served by the device's coherence point,
 // never by a stale line in this XCD's L2 (the cache-policy bit below; 16 bytes per access
 // through a buffer resource whose base is uniform over the workgroup).  These loads are not
-// cache hits, so a slot past S issues none.
+// cache hits, so a slot past S does not read split S - 1 again: its offset is moved past the
+// resource's range (at most 2^31 bytes), where a buffer load returns zeros without a memory
+// access, and no branch separates the loads.
 constexpr int kDeviceScopeLoad = 16;  // buffer-instruction cache policy: device scope
 constexpr uint32_t kRawBufferWord3 = 0x00020000;  // untyped 32-bit buffer, no swizzle
+constexpr uint32_t kPastRange = 0x80000000u;      // a buffer offset beyond every resource here
 struct CoherentPartials {
     __amdgpu_buffer_rsrc_t o_rsrc, ml_rsrc;
     uint32_t o_off;     // bytes from o_rsrc's base to this column of split 0
     uint32_t o_stride;  // bytes between consecutive splits
     uint32_t ml_off;    // bytes from ml_rsrc's base to (m, l) of split 0
+    // (m, l) of split s, zeros past S (never live: l = 0)
     __device__ __forceinline__ float2 ml_at(int s, int S) const {
-        if (s >= S) return make_float2(-INFINITY, 0.f);
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, ml_off + (uint32_t)s * 8u,
-                                                            0, kDeviceScopeLoad);
+        const uint32_t off = (s < S) ? ml_off + (uint32_t)s * 8u : kPastRange;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, off, 0, kDeviceScopeLoad);
         return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
     }
+    // this column of O_s, zeros past S
     __device__ __forceinline__ float4 o_at(int s, int S) const {
-        if (s >= S) return make_float4(0.f, 0.f, 0.f, 0.f);
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(o_rsrc, o_off + (uint32_t)s * o_stride,
-                                                             0, kDeviceScopeLoad);
+        const uint32_t off = (s < S) ? o_off + (uint32_t)s * o_stride : kPastRange;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(o_rsrc, off, 0, kDeviceScopeLoad);
         return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
                            __uint_as_float(v[3]));
     }
@@ -160,11 +190,19 @@ struct OwnPartial {
     }
 };
 
-// Merge of one (sequence, head) row's split partials for one float4 column of the output.
-// One pass with a running maximum: every load of a chunk is issued before any of its values
-// is used, so a chunk costs one memory round trip.  Idle splits (l_s = 0) contribute nothing,
-// whatever their O holds.  The merge kernel and the fused decode both call it, with the same
-// arithmetic whatever the source, so both give the same bits.
+// The merged column: acc / L, or zeros when no split saw a position.  Adding +0 makes a zero
+// result +0 whatever the signs of the zero terms that formed it, so merges that skip an
+// idle split and merges that add its zero product give the same bits.
+__device__ __forceinline__ float4 merge_finish(float4 acc, float L) {
+    if (!(L > 0.f)) return make_float4(0.f, 0.f, 0.f, 0.f);
+    return make_float4(acc.x / L + 0.f, acc.y / L + 0.f, acc.z / L + 0.f, acc.w / L + 0.f);
+}
+
+// Merge of one (sequence, head) row's split partials for one float4 column of the output,
+// by one lane on its own (the single-split step, whose one partial is in registers).  One
+// pass with a running maximum; idle splits (l_s = 0) contribute nothing, whatever their O
+// holds.  merge_row below is the same arithmetic shared over a row's lanes, and gives the
+// same bits.
 template <typename Src>
 __device__ __forceinline__ float4 merge_splits(const Src& src, int S) {
     float M = -INFINITY;
@@ -204,8 +242,85 @@ __device__ __forceinline__ float4 merge_splits(const Src& src, int S) {
         }
         M = Mn;
     }
-    if (!(L > 0.f)) return make_float4(0.f, 0.f, 0.f, 0.f);
-    return make_float4(acc.x / L, acc.y / L, acc.z / L, acc.w / L);
+    return merge_finish(acc, L);
+}
+
+// The same merge computed by the N consecutive lanes of one wave that own a row (N = D / 4;
+// lane c of them produces float4 column c).  Per chunk of 32 splits, every lane requests its
+// column's 32 O entries and the (m, l) of the chunk's splits it owns (c, c + N, ...), all
+// before any is used (one memory round trip); one cross-lane maximum gives the chunk's
+// maximum; the owning lane computes each split's weight exp(m_s - M) once and passes it with
+// l_s through the row's 32 LDS slots xw (float2, used by this row's lanes only), so the
+// other lanes spend five FMAs per split instead of an exponential and a maximum.  The
+// operations and their order are merge_splits's, so the results are the same bits.
+// DEAD_FINITE: every O entry of an idle split is finite (partials written by the decode
+// itself), so adding its zero-weighted product needs no select.
+template <int N, bool DEAD_FINITE, typename Src>
+__device__ __forceinline__ float4 merge_row(const Src& src, int S, int c, float2* xw) {
+    constexpr int PER = N <= kMergeChunk ? kMergeChunk / N : 1;  // splits owned per lane
+    float M = -INFINITY;
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
+        float4 o[kMergeChunk];
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) o[k] = src.o_at(s0 + k, S);
+        float2 v[PER];
+        bool live[PER];
+        float cm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int k = c + i * N;
+            const bool mine = k < kMergeChunk;  // N = 64: lanes 32..63 own none
+            v[i] = mine ? src.ml_at(s0 + k, S) : make_float2(-INFINITY, 0.f);
+            live[i] = mine && (s0 + k < S) && v[i].y > 0.f;
+            cm = fmaxf(cm, live[i] ? v[i].x : -INFINITY);
+        }
+        cm = within_group_max<N>(cm);
+        // A chunk with nothing live leaves the state as it is (factor 1, zero weights).
+        const bool any = cm != -INFINITY;
+        const float Mn = any ? fmaxf(M, cm) : M;
+        const float r = any ? fast_exp2((M - Mn) * kLog2e) : 1.f;  // 0 while M is still -inf
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int k = c + i * N;
+            if (k < kMergeChunk)
+                xw[k] = make_float2(live[i] ? fast_exp2((v[i].x - Mn) * kLog2e) : 0.f,
+                                    live[i] ? v[i].y : 0.f);
+        }
+        wave_lds_order();
+        L *= r;
+        acc.x *= r;
+        acc.y *= r;
+        acc.z *= r;
+        acc.w *= r;
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; k += 2) {
+            const float4 p = *reinterpret_cast<const float4*>(xw + k);  // (w, l) of k, k + 1
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float w = h ? p.z : p.x;
+                const float l = h ? p.w : p.y;  // 0 for an idle or absent split
+                const float4 x = o[k + h];
+                L = fmaf(w, l, L);
+                if constexpr (DEAD_FINITE) {
+                    acc.x = fmaf(w, x.x, acc.x);
+                    acc.y = fmaf(w, x.y, acc.y);
+                    acc.z = fmaf(w, x.z, acc.z);
+                    acc.w = fmaf(w, x.w, acc.w);
+                } else {
+                    const bool lv = l > 0.f;
+                    acc.x = lv ? fmaf(w, x.x, acc.x) : acc.x;
+                    acc.y = lv ? fmaf(w, x.y, acc.y) : acc.y;
+                    acc.z = lv ? fmaf(w, x.z, acc.z) : acc.z;
+                    acc.w = lv ? fmaf(w, x.w, acc.w) : acc.w;
+                }
+            }
+        }
+        wave_lds_order();
+        M = Mn;
+    }
+    return merge_finish(acc, L);
 }
 
 // ---------------------------------------------------------------- launcher arguments

@@ -77,9 +77,13 @@ struct DecodeGeom {
 
 // Dynamic LDS of one workgroup: staged page ids, then per head and stream (wave x 16-lane
 // row) the reference maximum, the true maximum and the sum l, then per stream the GH x D
-// accumulators (padded by 16 bytes).
+// accumulators (padded by 16 bytes).  The last-split merge reuses it from the start: 32
+// float2 weight slots per row of D / 4 lanes (streams x 16 lanes in the workgroup).
 __host__ __device__ constexpr size_t decode_lds_bytes(int streams, int gh, int d) {
-    return (size_t)kTableCap * 4 + (size_t)streams * gh * 3 * 4 + (size_t)streams * (gh * d + 4) * 4;
+    const size_t state = (size_t)kTableCap * 4 + (size_t)streams * gh * 3 * 4 +
+                         (size_t)streams * (gh * d + 4) * 4;
+    const size_t merge = (size_t)streams * 16 / (d / 4) * kMergeChunk * 8;
+    return state > merge ? state : merge;
 }
 
 // ------------------------------------------------------------------ K/V row fragments
@@ -719,12 +723,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         src.ml_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.partial_ml + row0 * S * 2, 0,
                                                         nh * S * 8, kRawBufferWord3);
         src.o_stride = D * 4;
+        // The D4 lanes of a row merge it together, exchanging split weights through the
+        // row's slots at the start of LDS (free once the streams' state is merged).
+        float2* xw = reinterpret_cast<float2*>(lds) + (tid / D4) * kMergeChunk;
         for (int idx = tid; idx < nh * D4; idx += nthreads) {
             const int j = idx / D4;
             const int c = idx - j * D4;
             src.o_off = (uint32_t)((j * S * D + c * 4) * 4);
             src.ml_off = (uint32_t)(j * S * 8);
-            reinterpret_cast<float4*>(a.out)[(row0 + j) * D4 + c] = merge_splits(src, S);
+            reinterpret_cast<float4*>(a.out)[(row0 + j) * D4 + c] =
+                merge_row<D4, true>(src, S, c, xw);
         }
         if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
