@@ -270,21 +270,61 @@ def test_combine_synthetic_partials(d, S):
     B = 1 if S > 1024 else 3
     o, ml = wl.make_partials(rng, batch=B, hq=40, head_dim=d, num_splits=S, all_empty_rows=2)
     ref = oracle.combine(o, ml[..., 0], ml[..., 1])
-    out = torch.full((B, 40, d), float("nan"), device=DEV)
+    got = run_combine(o, ml)
+    assert np.all(got.reshape(-1, d)[:2] == 0.0), "all-idle rows must be zero"
+    err = np.abs(got - ref)
+    tol = combine_tolerance(o, ml)
+    assert np.all(err <= tol), f"combine d={d} S={S}: max err/tol {np.max(err / tol):.3f}"
+
+
+def run_combine(o, ml):
+    B, H, S, d = o.shape
+    out = torch.full((B, H, d), float("nan"), device=DEV)
     pa.paged_attn_combine(dev(o), dev(ml), out)
     torch.cuda.synchronize()
-    got = host(out)
-    assert np.all(got.reshape(-1, d)[:2] == 0.0), "all-idle rows must be zero"
-    # f32 sums over S splits: besides the 1e-5 floor, allow the summation bound
-    # 2 * S * 2^-24 * (sum_s w_s |O_s|) / (sum_s w_s l_s), w_s = exp(m_s - M), in f64.
-    m64, l64, o64 = ml[..., 0].astype(np.float64), ml[..., 1].astype(np.float64), o
-    M = np.max(np.where(l64 > 0, m64, -np.inf), axis=-1, keepdims=True)
-    with np.errstate(invalid="ignore"):
-        w = np.where(l64 > 0, np.exp(m64 - M), 0.0)
-        bound = (w[..., None] * np.abs(o64)).sum(-2) / np.maximum((w * l64).sum(-1), 1e-30)[..., None]
-    tol = 1e-5 + 2.0 * S * 2.0 ** -24 * np.nan_to_num(bound)
-    err = np.abs(got - ref)
-    assert np.all(err <= tol), f"combine d={d} S={S}: max err/tol {np.max(err / tol):.3f}"
+    return host(out)
+
+
+def combine_tolerance(o, ml):
+    """f32 sums over S splits: besides the 1e-5 floor, the summation bound
+    2 * S * 2^-24 * (sum_s w_s |O_s|) / (sum_s w_s l_s), w_s = exp(m_s - M), in f64."""
+    S = o.shape[-2]
+    m64, l64 = ml[..., 0].astype(np.float64), ml[..., 1].astype(np.float64)
+    live = l64 > 0
+    M = np.max(np.where(live, m64, -np.inf), axis=-1, keepdims=True)
+    with np.errstate(invalid="ignore", over="ignore"):
+        w = np.where(live, np.exp(m64 - M), 0.0)
+        ao = np.where(live[..., None], np.abs(o.astype(np.float64)), 0.0)
+        bound = (w[..., None] * ao).sum(-2) / np.maximum((w * l64).sum(-1), 1e-30)[..., None]
+    return 1e-5 + 2.0 * S * 2.0 ** -24 * np.nan_to_num(bound)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_combine_idle_contents_and_chunk_order(d):
+    """Splits are merged 32 at a time with a running maximum.  Rows whose splits 32..63 are
+    all idle (a chunk with nothing live between live ones), whose largest maximum first
+    appears in the last chunk, or in the first: within the oracle's bar.  An idle split's m
+    and O are never used: NaN in O and a huge m in every idle split give the same bits."""
+    S = 96
+    announce(f"combine idle contents and chunk order d={d}")
+    rng = wl.rng_for([410, d])
+    o, ml = wl.make_partials(rng, batch=2, hq=8, head_dim=d, num_splits=S, all_empty_rows=1)
+    ml[:, :4, 32:64, 0] = -np.inf
+    ml[:, :4, 32:64, 1] = 0.0
+    o[:, :4, 32:64, :] = 0.0
+    ml[:, 2:4, 90, :] = (40.0, 3.0)   # the row maximum appears in the last chunk
+    ml[:, 4:6, 5, :] = (40.0, 3.0)    # ... or in the first, far above the rest
+    ref = oracle.combine(o, ml[..., 0], ml[..., 1])
+    clean = run_combine(o, ml)
+    err = np.abs(clean - ref)
+    tol = combine_tolerance(o, ml)
+    assert np.all(err <= tol), f"combine d={d}: max err/tol {np.max(err / tol):.3f}"
+    assert np.all(clean[0, 0] == 0.0), "an all-idle row must be zero"
+    idle = ml[..., 1] == 0.0
+    o2, ml2 = o.copy(), ml.copy()
+    o2[idle] = np.nan
+    ml2[..., 0][idle] = 1e30
+    assert_bitwise(run_combine(o2, ml2), clean, f"combine d={d} with garbage in idle splits")
 
 
 # ----------------------------------------------------------------------------- prefill
