@@ -363,9 +363,15 @@ int paged_attn_prefill(const float* q, const void* k_pages, const void* v_pages,
     a.q_blocks = q_blocks;
     // One prompt at head_dim 64, two workgroups per CU: the order alternates direction every
     // CU-count workgroups, so each CU's second workgroup is one of the lightest blocks.
-    a.round_wgs = (num_segs == 1 && head_dim == 64) ? compute_units() : 0;
+    const int cus = compute_units();
+    a.round_wgs = (num_segs == 1 && head_dim == 64) ? cus : 0;
+    // Query blocks that hold rows: at most ceil(len / 16) per segment, and the segments
+    // share the total_tokens packed rows without overlap.
+    const int64_t blocks = std::min<int64_t>((int64_t)q_blocks * num_segs,
+                                             ((int64_t)total_tokens + 15) / 16 + num_segs - 1);
+    const bool dense = blocks * num_q_heads > 2 * (int64_t)cus;
     return launched(
-        pa::launch_prefill(a, kv_dtype, head_dim, q_blocks, (hipStream_t)stream), stream);
+        pa::launch_prefill(a, kv_dtype, head_dim, q_blocks, dense, (hipStream_t)stream), stream);
 }
 
 int kv_page_write(const void* k_new, const void* v_new, void* k_pages, void* v_pages,

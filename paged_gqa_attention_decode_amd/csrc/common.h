@@ -406,7 +406,7 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_dtype, int head_dim, bool f
                          hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int q_blocks,
-                          hipStream_t stream);
+                          bool dense, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 hipError_t launch_kv_write_rope(const KvRopeArgs& a, int kv_dtype, hipStream_t stream);
 

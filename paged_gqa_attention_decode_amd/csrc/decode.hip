@@ -40,7 +40,8 @@
 //         K/V into its page and merges: the partials leave by device-scope stores, one
 //         relaxed device-scope ticket per (sequence, KV head, head group) finds the last
 //         workgroup, and that one reloads the group's partials and merges them with the
-//         arithmetic of the separate merge kernel, so both paths give the same bits.  With
+//         arithmetic of the separate merge kernel (the D/4 lanes of an output row sharing
+//         each split's weight through LDS), so both paths give the same bits.  With
 //         one split there is nothing to gather: each workgroup stores its partial, applies
 //         that arithmetic to it in registers and writes the output, with no ticket.
 //   heads the host spreads a KV head's query heads over twice the workgroups when the grid

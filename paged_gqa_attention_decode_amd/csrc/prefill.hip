@@ -16,7 +16,9 @@
 //         and memory pipeline, and a CU holding two heavy blocks set the end).  8 waves
 //         per workgroup, all on the same 16 query rows of one head, held to 128 registers
 //         for D = 64 so that two workgroups share a CU and a whole 512-token prefill is
-//         resident at once (occupancy, not a second register set, hides the load latency).
+//         resident at once (occupancy, not a second register set, hides the load latency);
+//         an f32 grid of more than two workgroups per CU runs a build held to 85 registers,
+//         three workgroups per CU.
 //         The causal key range of the block is cut into 32-key tiles dealt round-robin to
 //         the 8 waves, starting at a block-dependent wave; the 8 partial softmax states
 //         merge through LDS at the end.  With a 16-bit pool a wave requests its next tile's
@@ -66,8 +68,14 @@ constexpr int kWaves = 8;
 constexpr int kRows = 16;         // query rows per workgroup
 constexpr int kTablePages = 1024; // page ids staged in LDS per slice of the key range
 
+// Waves per SIMD the registers are budgeted for: 4 at D = 64 (two workgroups per CU), 2 at
+// D = 128; the f32 pool at D = 64 also has a 6-wave build (three workgroups per CU, 77
+// registers, no spills) for grids too large to be resident at two per CU.
 template <typename KV, int D>
-__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 4 : 2)))
+constexpr int default_occupancy() { return D <= 64 ? 4 : 2; }
+
+template <typename KV, int D, int OCC>
+__global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
     prefill_kernel(PrefillArgs a) {
     using T = typename KV::storage;
     using Ops = TileOps<KV, D>;
@@ -278,10 +286,23 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     }
 }
 
+// dense: more (query block, head) workgroups have rows than two per CU can hold at once
+// (several prompts, or one long one).  Then the f32 D = 64 build at three workgroups per CU
+// runs, so that more of the grid is resident at once; the blocks of a smaller grid are
+// resident anyway and keep the larger register budget, whose schedule is faster per
+// workgroup.  Both builds perform the same operations in the same order, so a segment's bits
+// do not depend on which one ran.
 template <typename KV, int D>
-hipError_t launch_typed(const PrefillArgs& a, int q_blocks, hipStream_t stream) {
+hipError_t launch_typed(const PrefillArgs& a, int q_blocks, bool dense, hipStream_t stream) {
     const dim3 grid(q_blocks * a.num_q_heads, 1, a.num_segs);
-    hipLaunchKernelGGL((prefill_kernel<KV, D>), grid, dim3(kWaves * 64), 0, stream, a);
+    constexpr int OCC = default_occupancy<KV, D>();
+    if constexpr (std::is_same_v<KV, F32> && D == 64) {
+        if (dense) {
+            hipLaunchKernelGGL((prefill_kernel<KV, D, 6>), grid, dim3(kWaves * 64), 0, stream, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((prefill_kernel<KV, D, OCC>), grid, dim3(kWaves * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -290,15 +311,15 @@ hipError_t launch_typed(const PrefillArgs& a, int q_blocks, hipStream_t stream) 
 PA_DEFINE_TAKE_BAD_METADATA(take_bad_metadata_prefill, g_bad_metadata_prefill)
 
 hipError_t launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, int q_blocks,
-                          hipStream_t stream) {
+                          bool dense, hipStream_t stream) {
     if (head_dim == 64) {
-        if (kv_dtype == 0) return launch_typed<F32, 64>(a, q_blocks, stream);
-        if (kv_dtype == 1) return launch_typed<F16, 64>(a, q_blocks, stream);
-        return launch_typed<BF16, 64>(a, q_blocks, stream);
+        if (kv_dtype == 0) return launch_typed<F32, 64>(a, q_blocks, dense, stream);
+        if (kv_dtype == 1) return launch_typed<F16, 64>(a, q_blocks, dense, stream);
+        return launch_typed<BF16, 64>(a, q_blocks, dense, stream);
     }
-    if (kv_dtype == 0) return launch_typed<F32, 128>(a, q_blocks, stream);
-    if (kv_dtype == 1) return launch_typed<F16, 128>(a, q_blocks, stream);
-    return launch_typed<BF16, 128>(a, q_blocks, stream);
+    if (kv_dtype == 0) return launch_typed<F32, 128>(a, q_blocks, dense, stream);
+    if (kv_dtype == 1) return launch_typed<F16, 128>(a, q_blocks, dense, stream);
+    return launch_typed<BF16, 128>(a, q_blocks, dense, stream);
 }
 
 }  // namespace pa

@@ -130,13 +130,18 @@ def test_repeat_runs_bitwise_and_poison_stays_out():
     assert np.isfinite(a[0]).all() and np.isfinite(a[1]).all()
 
 
-def test_prefill_segment_isolation_bitwise():
+@pytest.mark.parametrize("seed,lens,starts", [(604, [17, 64, 129, 257], [0, 63, 255, 512]),
+                                              (605, [256, 256, 256, 256], [0, 0, 300, 0])],
+                         ids=["histories", "four_256"])
+def test_prefill_segment_isolation_bitwise(seed, lens, starts):
     """A segment's rows are identical whether it is prefilled alone or packed with others,
-    and whatever its physical pages are."""
-    announce("prefill segment isolation")
-    rng = wl.rng_for(604)
+    and whatever its physical pages are.  The four 256-token prompts fill more workgroups
+    than two per CU hold at once, so the packed call runs the f32 build budgeted for three
+    workgroups per CU and each prompt alone the two-per-CU build: the two must agree."""
+    announce(f"prefill segment isolation {lens} {starts}")
+    rng = wl.rng_for(seed)
     case = wl.make_prefill_case(rng, hq=12, hkv=3, head_dim=64, page_size=16, dtype="f32",
-                                lens=[17, 64, 129, 257], starts=[0, 63, 255, 512])
+                                lens=lens, starts=starts)
 
     def run(c):
         kp, vp = dev(c.k_pages, c.dtype), dev(c.v_pages, c.dtype)
@@ -151,7 +156,7 @@ def test_prefill_segment_isolation_bitwise():
 
     full = run(case)
     assert np.isfinite(full).all()
-    for i in range(4):
+    for i in range(len(lens)):
         start, n = int(case.seg_desc[i, 0]), int(case.seg_desc[i, 1])
         rows = slice(start, start + n)
         desc = case.seg_desc[i:i + 1].copy()
