@@ -365,6 +365,7 @@ int paged_attn_prefill(const float* q, const void* k_pages, const void* v_pages,
     // CU-count workgroups, so each CU's second workgroup is one of the lightest blocks.
     const int cus = compute_units();
     a.round_wgs = (num_segs == 1 && head_dim == 64) ? cus : 0;
+    a.rank_segs = (num_segs >= 2 && num_segs <= pa::kRankSegs) ? 1 : 0;
     // Query blocks that hold rows: at most ceil(len / 16) per segment, and the segments
     // share the total_tokens packed rows without overlap.
     const int64_t blocks = std::min<int64_t>((int64_t)q_blocks * num_segs,

@@ -373,7 +373,9 @@ struct PrefillArgs {
     int q_blocks;  // 16-row query blocks of the longest segment
     float qscale;  // scale * log2(e)
     int round_wgs;  // workgroups dealt per round in alternating order (0: heaviest first only)
+    int rank_segs;  // 1: segments taken heaviest first (2 .. kRankSegs segments), 0: in order
 };
+constexpr int kRankSegs = 16;  // most segments a prefill call ranks by their last position
 
 struct KvWriteArgs {
     const void* k_new;

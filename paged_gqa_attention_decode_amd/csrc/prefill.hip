@@ -13,7 +13,9 @@
 //         heaviest blocks are dispatched before the light ones fill in behind them.  For one
 //         prompt at D = 64 every second round of CU-count workgroups runs in reverse, so that
 //         a CU's two workgroups are a heavy and a light block (they share its matrix cores
-//         and memory pipeline, and a CU holding two heavy blocks set the end).  8 waves
+//         and memory pipeline, and a CU holding two heavy blocks set the end).  A call
+//         with 2 .. kRankSegs segments takes them heaviest first (by last position), so
+//         the longest histories are dispatched first whatever the descriptor order.  8 waves
 //         per workgroup, all on the same 16 query rows of one head, held to 128 registers
 //         for D = 64 so that two workgroups share a CU and a whole 512-token prefill is
 //         resident at once (occupancy, not a second register set, hides the load latency);
@@ -93,7 +95,32 @@ __global__ void __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_e
     const int g = lane >> 4;    // MFMA k-group: 4 lane groups of 16
     const int c16 = lane & 15;  // query row within the block (B/D operand column)
 
-    const int32_t* dsc = a.seg_desc + 4 * (size_t)blockIdx.z;
+    // The segment of this workgroup's z slot.  Ranked calls take the segments heaviest first
+    // (by last position, absolute start + length; ties by index; a segment the checks below
+    // skip last), so the blocks with the longest histories are dispatched first wherever
+    // their segment sits in the descriptor array.  A permutation of the work: every segment
+    // computes the same bits in any slot.  (The slot's descriptor is read once, after the
+    // ranking: reading the slot's own first and another after a move measured slower.)
+    int seg = (int)blockIdx.z;
+    if (a.rank_segs) {
+        const int cap0 = a.max_pages << a.page_shift;
+        int wt = -1;  // lane i: segment i's last position + 1, -1 if it is skipped
+        if (lane < a.num_segs) {
+            const int32_t* d = a.seg_desc + 4 * lane;
+            const int s0 = d[0], l0 = d[1], b0 = d[2], t0 = d[3];
+            if (s0 >= 0 && s0 < a.total_tokens && l0 > 0 && b0 >= 0 && b0 < cap0 && t0 >= 0 &&
+                t0 < a.num_tables)
+                wt = b0 + min(min(l0, a.total_tokens - s0), cap0 - b0);
+        }
+        int rk = 0;
+        for (int j = 0; j < a.num_segs; ++j) {
+            const int other = __builtin_amdgcn_readlane(wt, j);
+            rk += (other > wt || (other == wt && j < lane)) ? 1 : 0;
+        }
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < a.num_segs && rk == seg);
+        seg = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+    }
+    const int32_t* dsc = a.seg_desc + 4 * (size_t)seg;
     const int start = dsc[0];
     int len = dsc[1];
     const int a0 = dsc[2];

@@ -169,6 +169,38 @@ def test_prefill_segment_isolation_bitwise(seed, lens, starts):
         assert_bitwise(run(alone), full[rows], f"segment {i} alone vs packed")
 
 
+def test_prefill_segment_order_bitwise():
+    """A call with 2..16 segments takes them heaviest first (by last position, ties by
+    index).  Any order of the descriptors, with tied segments and an empty descriptor among
+    them, gives the same bits, and packed rows that no segment covers stay untouched."""
+    announce("prefill segment order")
+    rng = wl.rng_for(606)
+    case = wl.make_prefill_case(rng, hq=12, hkv=3, head_dim=64, page_size=16, dtype="f32",
+                                lens=[17, 64, 129, 257, 64], starts=[0, 63, 255, 512, 63],
+                                gap_rows=3)
+    kp, vp = dev(case.k_pages, case.dtype), dev(case.v_pages, case.dtype)
+    table = dev(case.page_table)
+    pa.kv_page_write(dev(case.k_new, case.dtype), dev(case.v_new, case.dtype), kp, vp, table,
+                     dev(case.token_table_index), dev(case.token_position))
+    empty = np.array([[0, 0, 0, 0]], dtype=np.int32)
+    base = np.concatenate([case.seg_desc, empty])
+
+    def run(desc):
+        out = torch.full(case.q.shape, float("nan"), device=DEV)
+        pa.paged_attn_prefill(dev(case.q), kp, vp, table, dev(np.ascontiguousarray(desc)),
+                              case.max_chunk_len, case.scale, out)
+        torch.cuda.synchronize()
+        return host(out)
+
+    ref = run(base)
+    covered = np.zeros(case.q.shape[0], dtype=bool)
+    for st, ln, _, _ in case.seg_desc.tolist():
+        covered[st:st + ln] = True
+    assert np.isfinite(ref[covered]).all() and np.isnan(ref[~covered]).all()
+    for perm in ([5, 4, 3, 2, 1, 0], [3, 5, 1, 0, 4, 2], [4, 1, 0, 5, 2, 3]):
+        assert_bitwise(run(base[perm]), ref, f"descriptor order {perm}")
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,d,S", [("f16", 40, 8, 128, 32), ("f32", 12, 3, 64, 7),
                                               ("bf16", 64, 8, 128, 1)])
 def test_empty_sequences_in_a_batch(dtype, hq, hkv, d, S):
