@@ -246,32 +246,32 @@ __device__ __forceinline__ float4 merge_splits(const Src& src, int S) {
 }
 
 // The same merge computed by the N consecutive lanes of one wave that own a row (N = D / 4;
-// lane c of them produces float4 column c).  Per chunk of 32 splits, every lane requests its
-// column's 32 O entries and the (m, l) of the chunk's splits it owns (c, c + N, ...), all
+// lane c of them produces float4 column c).  Per chunk of C splits, every lane requests its
+// column's C O entries and the (m, l) of the chunk's splits it owns (c, c + N, ...), all
 // before any is used (one memory round trip); one cross-lane maximum gives the chunk's
 // maximum; the owning lane computes each split's weight exp(m_s - M) once and passes it with
-// l_s through the row's 32 LDS slots xw (float2, used by this row's lanes only), so the
+// l_s through the row's LDS slots xw (float2, used by this row's lanes only), so the
 // other lanes spend five FMAs per split instead of an exponential and a maximum.  The
 // operations and their order are merge_splits's, so the results are the same bits.
 // DEAD_FINITE: every O entry of an idle split is finite (partials written by the decode
 // itself), so adding its zero-weighted product needs no select.
-template <int N, bool DEAD_FINITE, typename Src>
-__device__ __forceinline__ float4 merge_row(const Src& src, int S, int c, float2* xw) {
-    constexpr int PER = N <= kMergeChunk ? kMergeChunk / N : 1;  // splits owned per lane
+template <int N, bool DEAD_FINITE, int C, typename Src>
+__device__ __forceinline__ float4 merge_row_chunks(const Src& src, int S, int c, float2* xw) {
+    constexpr int PER = N <= C ? C / N : 1;  // splits owned per lane
     float M = -INFINITY;
     float L = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < S; s0 += kMergeChunk) {
-        float4 o[kMergeChunk];
+    for (int s0 = 0; s0 < S; s0 += C) {
+        float4 o[C];
 #pragma unroll
-        for (int k = 0; k < kMergeChunk; ++k) o[k] = src.o_at(s0 + k, S);
+        for (int k = 0; k < C; ++k) o[k] = src.o_at(s0 + k, S);
         float2 v[PER];
         bool live[PER];
         float cm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int k = c + i * N;
-            const bool mine = k < kMergeChunk;  // N = 64: lanes 32..63 own none
+            const bool mine = k < C;  // lanes past the chunk own none
             v[i] = mine ? src.ml_at(s0 + k, S) : make_float2(-INFINITY, 0.f);
             live[i] = mine && (s0 + k < S) && v[i].y > 0.f;
             cm = fmaxf(cm, live[i] ? v[i].x : -INFINITY);
@@ -284,7 +284,7 @@ __device__ __forceinline__ float4 merge_row(const Src& src, int S, int c, float2
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int k = c + i * N;
-            if (k < kMergeChunk)
+            if (k < C)
                 xw[k] = make_float2(live[i] ? fast_exp2((v[i].x - Mn) * kLog2e) : 0.f,
                                     live[i] ? v[i].y : 0.f);
         }
@@ -295,7 +295,7 @@ __device__ __forceinline__ float4 merge_row(const Src& src, int S, int c, float2
         acc.z *= r;
         acc.w *= r;
 #pragma unroll
-        for (int k = 0; k < kMergeChunk; k += 2) {
+        for (int k = 0; k < C; k += 2) {
             const float4 p = *reinterpret_cast<const float4*>(xw + k);  // (w, l) of k, k + 1
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -321,6 +321,16 @@ __device__ __forceinline__ float4 merge_row(const Src& src, int S, int c, float2
         M = Mn;
     }
     return merge_finish(acc, L);
+}
+
+// The chunk a merge of S splits runs in: 8 for S <= 8 (one chunk, whose unused slots would
+// only add zero terms), else 32.  Both sizes give the same bits for S <= 8, so the step and
+// the merge kernel agree whatever they pick.  (A 4- and a 16-split chunk as well measured no
+// faster, and the larger step kernel slowed the 32-split case.)
+template <int N, bool DEAD_FINITE, typename Src>
+__device__ __forceinline__ float4 merge_row(const Src& src, int S, int c, float2* xw) {
+    if (S <= 8) return merge_row_chunks<N, DEAD_FINITE, 8>(src, S, c, xw);
+    return merge_row_chunks<N, DEAD_FINITE, kMergeChunk>(src, S, c, xw);
 }
 
 // ---------------------------------------------------------------- launcher arguments
