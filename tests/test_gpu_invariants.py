@@ -172,7 +172,8 @@ def test_prefill_segment_isolation_bitwise(seed, lens, starts):
 def test_prefill_segment_order_bitwise():
     """A call with 2..16 segments takes them heaviest first (by last position, ties by
     index).  Any order of the descriptors, with tied segments and an empty descriptor among
-    them, gives the same bits, and packed rows that no segment covers stay untouched."""
+    them, gives the same bits, and packed rows that no valid segment covers (gaps, and the
+    rows of a descriptor naming a missing table) stay untouched."""
     announce("prefill segment order")
     rng = wl.rng_for(606)
     case = wl.make_prefill_case(rng, hq=12, hkv=3, head_dim=64, page_size=16, dtype="f32",
@@ -183,7 +184,11 @@ def test_prefill_segment_order_bitwise():
     pa.kv_page_write(dev(case.k_new, case.dtype), dev(case.v_new, case.dtype), kp, vp, table,
                      dev(case.token_table_index), dev(case.token_position))
     empty = np.array([[0, 0, 0, 0]], dtype=np.int32)
-    base = np.concatenate([case.seg_desc, empty])
+    # A descriptor naming a table that does not exist, over the gap rows after segment 0: it
+    # is skipped, so those rows stay untouched.
+    st0, ln0 = int(case.seg_desc[0, 0]), int(case.seg_desc[0, 1])
+    bad = np.array([[st0 + ln0, 2, 0, 99]], dtype=np.int32)
+    base = np.concatenate([case.seg_desc, empty, bad])
 
     def run(desc):
         out = torch.full(case.q.shape, float("nan"), device=DEV)
@@ -197,7 +202,7 @@ def test_prefill_segment_order_bitwise():
     for st, ln, _, _ in case.seg_desc.tolist():
         covered[st:st + ln] = True
     assert np.isfinite(ref[covered]).all() and np.isnan(ref[~covered]).all()
-    for perm in ([5, 4, 3, 2, 1, 0], [3, 5, 1, 0, 4, 2], [4, 1, 0, 5, 2, 3]):
+    for perm in ([6, 5, 4, 3, 2, 1, 0], [3, 5, 1, 6, 0, 4, 2], [4, 1, 0, 5, 2, 3, 6]):
         assert_bitwise(run(base[perm]), ref, f"descriptor order {perm}")
 
 
