@@ -149,7 +149,7 @@ int paged_attn_decode(const float* q, const void* k_pages, const void* v_pages,
  *   k_pages,v_pages written at that one slot per (sequence, KV head), read elsewhere
  *   partial_o, partial_ml  split workspace as for paged_attn_decode (left holding the
  *                   partials)
- *   counters        paged_attn_decode_fused_counters(...) uint32, device: zero before the
+ *   counters        paged_attn_decode_fused_counters(...) uint32 words, device: zero before the
  *                   first call; every call leaves them zero again (the last split of a group
  *                   resets its counter; with num_splits = 1 they are not touched), so the
  *                   buffer is reused without clearing.  One counter per (sequence, KV
@@ -169,8 +169,11 @@ int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new
                             int window, int num_splits, float* partial_o, float* partial_ml,
                             uint32_t* counters, float* out, void* stream);
 
-/* Number of uint32 counters paged_attn_decode_fused needs at any head_dim, or 0 for invalid
- * arguments: num_seqs * num_kv_heads * 2 * ceil((Hq/Hkv) / 8). */
+/* Number of uint32 words of counters paged_attn_decode_fused needs at any head_dim, or 0 for
+ * invalid arguments: num_seqs * num_kv_heads * 2 * ceil((Hq/Hkv) / 8) counters, each in a
+ * 128-byte line of its own (32 words), so that the tickets of different groups do not queue
+ * on one line.  The buffer's start must be 128-byte aligned for that (any device allocation
+ * is); it is correct at any 4-byte alignment. */
 size_t paged_attn_decode_fused_counters(int num_seqs, int num_q_heads, int num_kv_heads);
 
 /*
@@ -183,8 +186,9 @@ size_t paged_attn_decode_fused_counters(int num_seqs, int num_q_heads, int num_k
  * nothing and frees nothing.
  *   Limits: the split workspace (paged_attn_decode_workspace_bytes(num_seqs, num_q_heads,
  *   head_dim, num_splits), e.g. 8.5 MB for 16 sequences x 64 heads x 16 splits at head_dim
- *   128) must fit in 16 MiB - 64 KiB, and the counters (paged_attn_decode_fused_counters)
- *   in 64 KiB (16384 of them); a larger call returns PA_ESCRATCH and enqueues nothing.
+ *   128) must fit in 15 MiB, and the counters (paged_attn_decode_fused_counters words) in
+ *   1 MiB (8192 counters of 128 bytes); a larger call returns PA_ESCRATCH and enqueues
+ *   nothing.
  *   Sharing: every call on one GPU uses that GPU's array, which keeps the last call's partials.
  *   Calls that overlap in time on one GPU (different streams or host threads) race and give
  *   undefined results: enqueue them on one stream.  The counters start at zero and every call

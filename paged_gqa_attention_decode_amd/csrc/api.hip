@@ -33,7 +33,8 @@ int max_heads_per_wg(int kv_dtype, int head_dim) {
     return kv_dtype == PA_F32 ? 8 : kMaxHeadsPerWg;
 }
 // The single-launch step's counter buffer holds 2 * ceil(group / 8) counters per KV head
-// (paged_attn_decode_fused_counters), at least twice the head groups of any grid below.
+// (paged_attn_decode_fused_counters), at least twice the head groups of any grid below,
+// each in a 128-byte line of its own (kCounterStride words).
 constexpr int kCounterHeads = 8;
 
 // Compute units of the current device, read once per device (0 if the runtime cannot say).
@@ -234,7 +235,7 @@ size_t paged_attn_decode_fused_counters(int num_seqs, int num_q_heads, int num_k
         return 0;
     const int group = num_q_heads / num_kv_heads;
     const int head_groups = (group + kCounterHeads - 1) / kCounterHeads;
-    return (size_t)num_seqs * num_kv_heads * head_groups * 2;
+    return (size_t)num_seqs * num_kv_heads * head_groups * 2 * pa::kCounterStride;
 }
 
 int paged_attn_decode_fused(const float* q, const void* k_new, const void* v_new,

@@ -705,7 +705,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         // the workgroup counted; the last one counted reads after its count returned.
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        uint32_t* counter = a.counters + ((size_t)b * a.num_kv_heads + kvh) * a.head_groups + hg;
+        uint32_t* counter =
+            a.counters + (((size_t)b * a.num_kv_heads + kvh) * a.head_groups + hg) * kCounterStride;
         if (tid == 0) {
             const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);

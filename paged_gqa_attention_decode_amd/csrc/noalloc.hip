@@ -18,9 +18,10 @@ namespace pa {
 
 namespace {
 
-// The first 64 KiB hold the merge counters and nothing else: they start at zero (the array
-// is zero-filled) and every call leaves them at zero.  The rest holds a call's partials, up
-// to 16 MiB - 64 KiB: e.g. 16 sequences x 64 query heads x 16 splits at head_dim 128 (8.5 MB).
+// The first 1 MiB holds the merge counters and nothing else (8192 of them, one per 128-byte
+// line): they start at zero (the array is zero-filled) and every call leaves them at zero.
+// The rest holds a call's partials, up to 15 MiB: e.g. 16 sequences x 64 query heads x 16
+// splits at head_dim 128 (8.5 MB).
 static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 }  // namespace

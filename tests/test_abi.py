@@ -116,10 +116,10 @@ def test_decode_validation(kw, status):
 def test_fused_counters_and_validation():
     lib = pa.raw_library()
     # one per (sequence, KV head, group of 8 query heads), doubled to cover head_dim 256
-    # (groups of 4 there)
-    assert pa.paged_attn_decode_fused_counters(1, 40, 8) == 8 * 2
-    assert pa.paged_attn_decode_fused_counters(16, 64, 8) == 128 * 2
-    assert pa.paged_attn_decode_fused_counters(2, 12 * 16, 12) == 2 * 12 * 2 * 2   # G=16
+    # (groups of 4 there), each in a 128-byte line of its own (32 uint32 words)
+    assert pa.paged_attn_decode_fused_counters(1, 40, 8) == 8 * 2 * 32
+    assert pa.paged_attn_decode_fused_counters(16, 64, 8) == 128 * 2 * 32
+    assert pa.paged_attn_decode_fused_counters(2, 12 * 16, 12) == 2 * 12 * 2 * 2 * 32   # G=16
     assert pa.paged_attn_decode_fused_counters(1, 41, 8) == 0
     f = lib.paged_attn_decode_fused
     # (q, k_new, v_new, kp, vp, dtype, table, ctx, B, Hq, Hkv, D, ps, P, maxp, scale, window,
@@ -261,8 +261,9 @@ def test_noalloc_workspace_limits_are_checked_before_the_device():
     assert noalloc(B=-1) == pa.PA_EINVAL
     # 64 sequences x 64 heads x 512 splits x 130 floats = 1.09 GB of partials
     assert noalloc(B=64, Hq=64, Hkv=8, S=512) == pa.PA_ESCRATCH
-    # 20000 sequences x 8 KV heads x 2 counters = 320,000 counters > 16,384
-    assert noalloc(B=20000, Hq=8, Hkv=8, S=1, D=64) == pa.PA_ESCRATCH
+    # 1000 sequences x 8 KV heads x 2 counters = 16,000 counters > 8,192 (1 MiB of 128-byte
+    # counter lines); the partials (1000 x 8 x 130 floats) would fit
+    assert noalloc(B=1000, Hq=8, Hkv=8, S=1, D=128) == pa.PA_ESCRATCH
     assert noalloc(B=0) == pa.PA_OK
 
 
