@@ -176,6 +176,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         }
     }
     int b = blockIdx.z;
+    // In grid order the query is requested right after the table, ahead of the length and
+    // the current token's page id (two dependent scalar round trips), so that its round trip
+    // overlaps theirs; a ranked workgroup knows its sequence only after the ranking.  Columns
+    // past the workgroup's heads get a zero query (their scores are computed and never
+    // stored); it is scaled by scale * log2(e) after the table is staged.
+    typename Ops::QRaw qraw;
+    if constexpr (!RANKED)
+        qraw = Ops::fetch_q(a.q + ((size_t)b * a.num_q_heads + h0 + min(c16, nh - 1)) * D, g);
     int raw_len;
     if constexpr (RANKED) {
         // Lane j holds sequence j's length; its rank orders the batch by attended length,
@@ -236,11 +244,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
             if (pid >= 0 && pid < a.num_pages) t_new = raw - 1;
         }
     }
-    // The query of the lane's column is requested before the table is staged, so its round
-    // trip overlaps the table's; it is scaled by scale * log2(e) afterwards.  Columns past
-    // the workgroup's heads get a zero query (their scores are computed and never stored).
-    const typename Ops::QRaw qraw =
-        Ops::fetch_q(a.q + ((size_t)b * a.num_q_heads + h0 + min(c16, nh - 1)) * D, g);
+    if constexpr (RANKED)
+        qraw = Ops::fetch_q(a.q + ((size_t)b * a.num_q_heads + h0 + min(c16, nh - 1)) * D, g);
     if (whole_row) {
 #pragma unroll
         for (int k = 0; k < TPT; ++k) {
