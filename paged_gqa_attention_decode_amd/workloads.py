@@ -137,7 +137,7 @@ WORKLOADS = {
     # 256 MB last-level cache), cycled step by step, so the step's K/V comes from HBM.
     "decode_hq28_hkv4_d128_ctx1641_f16": Workload(
         name="decode_hq28_hkv4_d128_ctx1641_f16", kind="decode", index=3, hq=28, hkv=4,
-        head_dim=128, page_size=16, dtype="f16", ctx=(1641,), num_splits=16, layers=28,
+        head_dim=128, page_size=16, dtype="f16", ctx=(1641,), num_splits=32, layers=28,
         rotations=4, description="7B-shape decode, batch 1, 28 layers per step"),
     "decode_b16_hq64_hkv8_d128_ctx64to4096_bf16": Workload(
         name="decode_b16_hq64_hkv8_d128_ctx64to4096_bf16", kind="decode", index=4, hq=64,
@@ -153,7 +153,7 @@ WORKLOADS = {
         description="the continuous-batching decode with a 1024-position sliding window"),
     "decode_hq16_hkv8_d256_ctx4096_bf16": Workload(
         name="decode_hq16_hkv8_d256_ctx4096_bf16", kind="decode", index=6, hq=16, hkv=8,
-        head_dim=256, page_size=16, dtype="bf16", ctx=(4096,), num_pages=256, num_splits=24,
+        head_dim=256, page_size=16, dtype="bf16", ctx=(4096,), num_pages=256, num_splits=32,
         layers=16, description="head_dim-256 decode, batch 1, 16 layers per step"),
     # The 512-token prefill in crucible's production GQA geometry (12 query heads over 3 kv
     # heads) with a bf16 pool: the measurement shape of the 16-bit MFMA prefill.
