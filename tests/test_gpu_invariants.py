@@ -169,6 +169,26 @@ def test_prefill_segment_isolation_bitwise(seed, lens, starts):
         assert_bitwise(run(alone), full[rows], f"segment {i} alone vs packed")
 
 
+def test_fused_counters_at_any_word_alignment():
+    """Each ticket counter has a 128-byte line of its own when the counter buffer starts on
+    one; a buffer that starts at any 4-byte offset gives the same bits (only the spacing
+    changes), and is left at zero."""
+    announce("fused step with an offset counter buffer")
+    rng = wl.rng_for(611)
+    case = wl.make_decode_case(rng, batch=3, hq=40, hkv=8, head_dim=128, page_size=16,
+                               dtype="f16", ctx=[3254, 17, 900], num_splits=32)
+    ref = DecodeRun(case, num_splits=32).fused_step()
+    run = DecodeRun(case, num_splits=32)
+    B, Hq, _ = case.q.shape
+    n = pa.paged_attn_decode_fused_counters(B, Hq, case.k_pages.shape[2])
+    backing = torch.zeros(n + 7, dtype=torch.int32, device=DEV)
+    run.counters = backing[5:5 + n]
+    assert run.counters.data_ptr() % 128 != 0
+    assert_bitwise(run.fused_step(), ref, "offset counters vs aligned")
+    assert_bitwise(run.fused_step(), ref, "offset counters, second call")
+    assert int(backing.abs().sum().item()) == 0, "counters must be left at zero"
+
+
 def test_prefill_segment_order_bitwise():
     """A call with 2..16 segments takes them heaviest first (by last position, ties by
     index).  Any order of the descriptors, with tied segments and an empty descriptor among
